@@ -1,0 +1,5 @@
+"""fp64 CPU oracle of the verification sampler. Test infrastructure only: used by tests/, the
+smoke check and the benchmark's CPU-baseline leg, never by the product path."""
+from .oracle import (Result, verify, verify_workload, tempered_log_softmax, softmax, accepts,
+                     residual_weights, inverse_cdf, accept_window_measure, FLAG_TOL,
+                     FINAL_WINDOW_MEASURE)
