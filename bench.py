@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-decoding verification sampler on one MI355X.
+
+One step = one spec_verify call over one batch (row statistics, accept scan and final draw for
+every sequence). Default workload: B=64 sequences, D=7 draft positions, V=128256, bf16 logits,
+T=1, Zipf(1.1)+N(0,1) target and target+N(0,1) draft (seed 0). Several copies of the inputs
+are resident in HBM and rotated so that no step can be served from the 256 MB Infinity Cache.
+
+Prints ONE JSON line: verified rows/s (sequences per second) as `value`, the HBM bandwidth of
+the algorithmic bytes, the roofline of the dominant kernel (row statistics) timed with HIP
+events on the launch stream, and the fp64 CPU oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified rows/s + HBM GB/s (% of peak), B=64 D=7 V=128256 bf16"
+HBM_PEAK_GBPS = 8000.0
+SRC = os.path.join(ROOT, "sampling_spec_verify_02_amd", "csrc", "spec_verify.hip")
+TRAFFIC = os.path.join(ROOT, "profiles", "traffic_row_stats_c3.json")
+
+WORKLOADS = {
+    "c1": "B=1 D=4 V=1024 fp32 T=1, N(0,2^2) target, draft +N(0,0.5^2)",
+    "c2": "B=16 D=4 V=32000 fp32 T=1, Zipf(1.1)+N(0,1) target, draft +N(0,1)",
+    "c3": "B=64 D=7 V=128256 bf16 T=1, Zipf(1.1)+N(0,1) target, draft +N(0,1)",
+    "c4": "B=256 D=3 V=128256 bf16, half greedy / half T=0.7, 10% draft==target, else +N(0,1.5^2)",
+    "c5": "B=512 D=7 V=129280 bf16 T=1, ragged L~U{1..7}, draft sigma_b~U[0.25,2]",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def valid_row_bytes(w) -> int:
+    """Algorithmic logit bytes: every row the method needs, once (target rows 0..L_b, draft rows
+    0..L_b-1, no draft rows for greedy sequences)."""
+    rows = 0
+    for b in range(w.B):
+        L = int(w.lens[b])
+        rows += (L + 1) + (0 if w.temperature[b] == 0 else L)
+    return rows * w.V * w.elem_bytes, rows
+
+
+def source_digest() -> str:
+    return hashlib.sha256(open(SRC, "rb").read()).hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per launch of the row-statistics kernel from the committed rocprofv3 PMC
+    summary, or None if the kernel source changed since the counters were taken."""
+    try:
+        t = json.load(open(TRAFFIC))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_digest():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float):
+    from oracle import verify
+
+    tgt, drf = w.target_f32(), w.draft_f32()
+    lens = w.lens if w.lens_given else None
+
+    def run(k):
+        t0 = time.perf_counter()
+        verify(tgt[:k], drf[:k], w.tokens[:k], None if lens is None else lens[:k],
+               w.uniforms[:k], w.temperature[:k])
+        return time.perf_counter() - t0
+
+    per = run(min(2, w.B)) / min(2, w.B)
+    k = int(max(1, min(w.B, seconds / max(per, 1e-6))))
+    reps, dt = 0, 0.0
+    while True:                      # whole-batch repeats until the sample is ~`seconds` long
+        dt += run(k)
+        reps += 1
+        if dt >= seconds or k < w.B or reps >= 1000:
+            break
+    try:
+        model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                     if l.startswith("model name"))
+    except (OSError, StopIteration):
+        model = platform.processor()
+    return {"value": reps * k / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} x first {k} of {w.B} sequences of the same workload, numpy fp64, "
+                      f"one thread, {dt:.1f} s on {model} "
+                      f"({len(os.sched_getaffinity(0))} cores visible)",
+            "ms_per_call_extrapolated": 1000 * dt / (reps * k) * w.B}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (sequences shard over B with no "
+              "exchange; multi-GPU runs are not part of it). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sampling_spec_verify_02_amd as sv
+    from workloads import make
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"bench: generating {args.config} seed {args.seed}")
+    w = make(args.config, args.seed)
+    alg_bytes, rows = valid_row_bytes(w)
+
+    def logits(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    ncopy = max(1, args.copies)
+    tgts = [logits(w.target) for _ in range(ncopy)]
+    drfs = [logits(w.draft) for _ in range(ncopy)]
+    tok = torch.from_numpy(w.tokens).to(dev)
+    lens = torch.from_numpy(w.lens).to(dev) if w.lens_given else None
+    uni = torch.from_numpy(w.uniforms).to(dev)
+    temp = torch.from_numpy(w.temperature).to(dev)
+    al = torch.empty(w.B, dtype=torch.int32, device=dev)
+    out = torch.empty((w.B, w.D + 1), dtype=torch.int32, device=dev)
+    lib = sv.lib()
+    fn = lib.spec_verify_bf16 if w.dtype == "bf16" else lib.spec_verify_f32
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)  # noqa: E731
+    calls = [(P(tgts[c]), P(drfs[c]), P(tok), P(lens), P(uni), w.B, w.D, w.V, P(temp), P(al),
+              P(out), sp) for c in range(ncopy)]
+
+    def step(k):
+        rc = fn(*calls[k % ncopy])
+        if rc != 0:
+            raise RuntimeError(f"spec_verify failed: {sv.strerror(rc)}")
+
+    # correctness of the benchmarked call against the oracle on this workload
+    step(0)
+    torch.cuda.synchronize()
+    from oracle import verify_workload
+    ref = verify_workload(w)
+    g_al, g_tok = al.cpu().numpy(), out.cpu().numpy()
+    ok = ~ref.flagged
+    mism = int(np.sum(ok & ((g_al != ref.accept_len) | np.any(g_tok != ref.tokens, axis=1))))
+    log(f"bench: parity vs oracle on the benched batch: {mism} unflagged mismatches "
+        f"({int(ref.flagged.sum())} flagged rows)")
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronised on both sides
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for k in range(K):
+        step(k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1000.0 * wall / K
+    ev_ms_step = e0.elapsed_time(e1) / K
+
+    # the dominant kernel's duration, with HIP events on its launch stream (same K steps again)
+    rc = lib.spec_verify_profile_start(K)
+    if rc != 0:
+        raise RuntimeError(sv.strerror(rc))
+    for k in range(K):
+        step(k)
+    durs = (ctypes.c_float * K)()
+    n = ctypes.c_int(0)
+    rc = lib.spec_verify_profile_stop(durs, K, ctypes.byref(n))
+    if rc != 0:
+        raise RuntimeError(sv.strerror(rc))
+    kern_ms = float(np.mean(np.array(durs[:n.value], dtype=np.float64)))
+    kern_gbps = alg_bytes / (kern_ms * 1e-3) / 1e9
+
+    gbps = alg_bytes / (ms_step * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": w.B / (ms_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {WORKLOADS[args.config]}", "B": w.B, "D": w.D,
+                   "V": w.V, "seed": args.seed, "input_copies_rotated": ncopy},
+        "hbm_gbps": gbps,
+        "pct_of_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
+        "logit_rows_per_s": rows / (ms_step * 1e-3),
+        "algorithmic_bytes_per_step": alg_bytes,
+        "event_ms_per_step": ev_ms_step,
+        "mean_accept_len": float(g_al.mean()),
+        "parity_unflagged_mismatches": mism,
+        "roofline": {"bound": "hbm", "kernel": "row_stats_kernel", "achieved": kern_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": kern_gbps / HBM_PEAK_GBPS,
+                     "traffic": read_traffic(), "kernel_ms": kern_ms},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

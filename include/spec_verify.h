@@ -1,0 +1,136 @@
+/*
+ * spec_verify.h - C ABI of the speculative-decoding verification sampler for MI355X (gfx950).
+ *
+ * The operation (defined on the pages "Speculative Speculative Decoding - асинхронизируй это",
+ * SD recap: accept / reject / residual rule; "Accélérer Sonar par la Spéculation", sections
+ * "Décodage spéculatif" and "Cible-Brouillon": n drafts give up to n + 1 tokens, the target's
+ * logits after the accepted prefix are sampled for one more; "NVIDIA: öt irányelv ...",
+ * section "Mit csinál a spekulatív dekódolás?": in-order acceptance up to the first mismatch,
+ * AL in [1, 1 + D]):
+ *
+ *   For each sequence b with draft length L = L_b and temperature T = T_b:
+ *     T > 0:  p_i = softmax(target[b][i] / T), q_i = softmax(draft[b][i] / T).
+ *             For i = 0 .. L-1: accept draft token x_i iff u[b][i] < min(1, p_i(x_i)/q_i(x_i));
+ *             stop at the first rejection j and draw the token at j from
+ *             norm(max(0, p_j - q_j)); if all L are accepted, draw a bonus token from p_L.
+ *             The draw is an inverse CDF in ascending token id with the uniform u[b][D]:
+ *             the smallest k with sum_{v<=k} w_v > u[b][D] * sum_v w_v.
+ *     T == 0: greedy: accept x_i iff x_i is the target argmax at i (lowest index on ties);
+ *             emit the target argmax at the first mismatch, or at position L if all match.
+ *   AL = (number of accepted drafts) + 1, in [1, L + 1].
+ *
+ * Memory: every pointer argument except `workspace`-less host scalars is DEVICE memory owned
+ * by the caller, row-major and contiguous. Nothing is retained after the call's stream work
+ * completes. The call only enqueues work on `stream` (NULL = the default stream) and never
+ * synchronizes; read the outputs after synchronizing that stream.
+ *
+ * Layouts (e = 2 bytes for bf16, 4 for fp32; target and draft share one dtype):
+ *   target_logits  [B][D+1][V]  target logits at the D draft positions and the tail position.
+ *   draft_logits   [B][D][V]    draft logits at the D draft positions.
+ *   draft_tokens   [B][D]       int32; entries at positions >= L_b are ignored.
+ *   draft_lens     [B]          int32 L_b in [0, D]; NULL means every L_b = D. Rows at target
+ *                               positions > L_b and draft positions >= L_b are never read.
+ *   uniforms       [B][D+1]     fp32 in [0, 1): columns 0..D-1 are the accept tests of
+ *                               positions 0..D-1, column D is the final-draw uniform.
+ *   temperature    [B]          fp32; 0 = greedy, > 0 sampled.
+ *   out_accept_len [B]          int32 AL; 0 marks a row whose inputs are invalid.
+ *   out_tokens     [B][D+1]     int32; the first AL entries are the emitted tokens
+ *                               (accepted drafts, then the final token), the rest -1.
+ *
+ * Errors:
+ *   - Problems visible on the host return a negative sv_status and enqueue nothing:
+ *     a NULL required pointer, B <= 0, D < 0, V <= 0, D > SV_MAX_D, or sizes whose element
+ *     counts overflow 64 bits.
+ *   - Per-row data errors found on the device mark only that row (AL = 0, tokens -1):
+ *     L_b outside [0, D], T_b negative, NaN or infinite, a draft token outside [0, V) at a
+ *     position < L_b.
+ *   - A failed launch or allocation returns SV_EHIP / SV_ENOMEM.
+ *   - Logits must be finite in every row that is read; other values give unspecified tokens
+ *     (never an out-of-bounds access).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SV_OK = 0,
+  SV_EINVAL = -1,   /* bad argument (NULL pointer, size out of range) */
+  SV_EDTYPE = -2,   /* unknown dtype code */
+  SV_EHIP = -3,     /* a HIP runtime call or kernel launch failed */
+  SV_ENODEV = -4,   /* no usable gfx950 device */
+  SV_ENOMEM = -5,   /* workspace allocation failed or caller workspace too small */
+} sv_status;
+
+#define SV_MAX_D 64   /* largest draft length D accepted */
+
+/* bf16 logits (bit patterns of bfloat16, 2 bytes each). Returns SV_OK or a negative sv_status.
+ * Uses a library-owned workspace on the current device, allocated on first use and grown
+ * when a larger problem arrives (hipMalloc; calls on one device are serialized by a mutex
+ * while they enqueue). */
+int spec_verify_bf16(const void* target_logits, const void* draft_logits,
+                     const int32_t* draft_tokens, const int32_t* draft_lens,
+                     const float* uniforms, int B, int D, int V,
+                     const float* temperature, int32_t* out_accept_len,
+                     int32_t* out_tokens, hipStream_t stream);
+
+/* Same operation on fp32 logits. */
+int spec_verify_f32(const void* target_logits, const void* draft_logits,
+                    const int32_t* draft_tokens, const int32_t* draft_lens,
+                    const float* uniforms, int B, int D, int V,
+                    const float* temperature, int32_t* out_accept_len,
+                    int32_t* out_tokens, hipStream_t stream);
+
+/* Bytes of device workspace one call of shape (B, D, V) needs (0 on bad sizes). */
+size_t spec_verify_workspace_bytes(int B, int D, int V);
+
+/* Same operation with caller-provided device workspace of at least
+ * spec_verify_workspace_bytes(B, D, V) bytes, 256-byte aligned. dtype: 0 = fp32, 1 = bf16.
+ * Nothing is allocated. The workspace must not be used by another call until this call's
+ * stream work has completed. */
+int spec_verify_ws(int dtype, const void* target_logits, const void* draft_logits,
+                   const int32_t* draft_tokens, const int32_t* draft_lens,
+                   const float* uniforms, int B, int D, int V,
+                   const float* temperature, int32_t* out_accept_len,
+                   int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/* Same operation, also exporting the per-row statistics the kernels computed (for tests).
+ * Any export pointer may be NULL. Unused rows hold NaN / -1.
+ *   row_stats   [B][2D+1][2] fp32: (max of logits/T, ln sum exp(logits/T - max)) for target
+ *               rows 0..D then draft rows 0..D-1 (sampled sequences).
+ *   row_argmax  [B][D+1] int32: target argmax per position (greedy sequences).
+ *   logpq_x     [B][D][2] fp32: (log p_i(x_i), log q_i(x_i)) at the tested positions. */
+int spec_verify_debug(int dtype, const void* target_logits, const void* draft_logits,
+                      const int32_t* draft_tokens, const int32_t* draft_lens,
+                      const float* uniforms, int B, int D, int V,
+                      const float* temperature, int32_t* out_accept_len,
+                      int32_t* out_tokens, float* row_stats, int32_t* row_argmax,
+                      float* logpq_x, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* spec_verify_strerror(int code);
+
+/* Library ABI version (major * 100 + minor). */
+int spec_verify_version(void);
+
+/* Timing hook for benchmarks. spec_verify_profile_start(n) creates n event pairs on the current
+ * device; each following call (any entry point, up to n calls) records one pair around its
+ * row-statistics kernel on the call's stream. spec_verify_profile_stop waits for those events,
+ * writes up to max_out durations in milliseconds to the host array out_ms (may be NULL), the
+ * number of recorded calls to *n_recorded, and releases the events. Returns SV_EINVAL if not
+ * started (stop) or already started (start), SV_EHIP on a runtime failure. */
+int spec_verify_profile_start(int max_calls);
+int spec_verify_profile_stop(float* out_ms, int max_out, int* n_recorded);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

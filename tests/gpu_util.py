@@ -1,0 +1,55 @@
+"""Helpers of the GPU tests: move a seeded workload to the device, run the HIP path through the
+C ABI, and compare its outputs with the oracle's."""
+import numpy as np
+import torch
+
+import sampling_spec_verify_02_amd as sv
+
+
+def device():
+    return torch.device("cuda:0")
+
+
+def logits_to_dev(arr, dtype, dev):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(dev)
+
+
+def to_dev(w, dev=None, lens=None):
+    dev = dev or device()
+    return dict(
+        target=logits_to_dev(w.target, w.dtype, dev),
+        draft=logits_to_dev(w.draft, w.dtype, dev),
+        tokens=torch.from_numpy(np.ascontiguousarray(w.tokens)).to(dev),
+        lens=(torch.from_numpy(w.lens).to(dev) if (w.lens_given if lens is None else lens)
+              else None),
+        uniforms=torch.from_numpy(np.ascontiguousarray(w.uniforms)).to(dev),
+        temperature=torch.from_numpy(np.ascontiguousarray(w.temperature)).to(dev),
+    )
+
+
+def run(w, dev=None, debug=False, workspace=None):
+    t = to_dev(w, dev)
+    args = (t["target"], t["draft"], t["tokens"], t["lens"], t["uniforms"], t["temperature"])
+    if debug:
+        out = sv.spec_verify_debug(*args)
+    else:
+        out = sv.spec_verify(*args, workspace=workspace)
+    torch.cuda.synchronize()
+    return tuple(o.cpu().numpy() for o in out)
+
+
+def compare(ref, al, toks, label=""):
+    """Bit-exact on every row the oracle did not flag. Returns (#flagged, #mismatched flagged)."""
+    ok = ~ref.flagged
+    bad = np.nonzero(ok & ((al != ref.accept_len) | np.any(toks != ref.tokens, axis=1)))[0]
+    if bad.size:
+        b = bad[0]
+        raise AssertionError(
+            f"{label}: {bad.size} unflagged rows differ; first b={b}: gpu AL={al[b]} "
+            f"tokens={toks[b].tolist()} oracle AL={ref.accept_len[b]} "
+            f"tokens={ref.tokens[b].tolist()} mode={ref.final_mode[b]}")
+    fl = ref.flagged
+    mism = int(np.sum(fl & ((al != ref.accept_len) | np.any(toks != ref.tokens, axis=1))))
+    return int(fl.sum()), mism

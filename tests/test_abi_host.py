@@ -1,0 +1,100 @@
+"""The C-ABI library loads, exports every symbol include/spec_verify.h declares, and rejects bad
+arguments on the host before touching any device."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from sampling_spec_verify_02_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(spec_verify\w*)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for must in ("spec_verify_bf16", "spec_verify_f32", "spec_verify_ws",
+                 "spec_verify_workspace_bytes", "spec_verify_debug", "spec_verify_strerror"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, name
+
+
+def test_static_queries():
+    lib = _lib.lib()
+    assert lib.spec_verify_version() >= 100
+    assert lib.spec_verify_workspace_bytes(64, 7, 128256) > 0
+    assert lib.spec_verify_workspace_bytes(0, 7, 128256) == 0
+    assert lib.spec_verify_workspace_bytes(4, -1, 10) == 0
+    assert lib.spec_verify_workspace_bytes(4, _lib.SV_MAX_D + 1, 10) == 0
+    assert lib.spec_verify_workspace_bytes(4, 2, 0) == 0
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(_lib.strerror(code), str)
+
+
+FAKE = ctypes.c_void_p(4096)      # never dereferenced: every case fails before any launch
+NUL = ctypes.c_void_p(0)
+
+
+def _call(fn, B=2, D=3, V=100, t=FAKE, d=FAKE, tok=FAKE, u=FAKE, temp=FAKE, ol=FAKE, ot=FAKE):
+    lib = _lib.lib()
+    if fn == "ws":
+        return lib.spec_verify_ws(1, t, d, tok, NUL, u, B, D, V, temp, ol, ot, FAKE, 1 << 30, NUL)
+    return getattr(lib, fn)(t, d, tok, NUL, u, B, D, V, temp, ol, ot, NUL)
+
+
+@pytest.mark.parametrize("fn", ["spec_verify_bf16", "spec_verify_f32", "ws"])
+def test_bad_arguments_return_einval(fn):
+    E = _lib.SV_EINVAL
+    assert _call(fn, B=0) == E
+    assert _call(fn, B=-3) == E
+    assert _call(fn, D=-1) == E
+    assert _call(fn, D=_lib.SV_MAX_D + 1) == E
+    assert _call(fn, V=0) == E
+    assert _call(fn, t=NUL) == E
+    assert _call(fn, d=NUL) == E
+    assert _call(fn, tok=NUL) == E
+    assert _call(fn, u=NUL) == E
+    assert _call(fn, temp=NUL) == E
+    assert _call(fn, ol=NUL) == E
+    assert _call(fn, ot=NUL) == E
+    assert _call(fn, B=1 << 30, D=63, V=1 << 30) == E      # element count overflow guard
+
+
+def test_bad_dtype_and_workspace():
+    lib = _lib.lib()
+    args = (FAKE, FAKE, FAKE, NUL, FAKE, 2, 3, 100, FAKE, FAKE, FAKE)
+    assert lib.spec_verify_ws(7, *args, FAKE, 1 << 30, NUL) == _lib.SV_EDTYPE
+    assert lib.spec_verify_ws(1, *args, NUL, 1 << 30, NUL) == _lib.SV_EINVAL
+    assert lib.spec_verify_ws(1, *args, FAKE, 16, NUL) == _lib.SV_ENOMEM
+    assert lib.spec_verify_ws(1, *args, ctypes.c_void_p(4096 + 8), 1 << 30, NUL) == _lib.SV_ENOMEM
+
+
+def test_d0_allows_null_draft_pointers():
+    lib = _lib.lib()
+    # D = 0: draft logits and tokens are not needed; with no device the call ends in ENODEV
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a device is present: this host-only case would launch")
+    rc = lib.spec_verify_bf16(FAKE, NUL, NUL, NUL, FAKE, 2, 0, 100, FAKE, FAKE, FAKE, NUL)
+    assert rc == _lib.SV_ENODEV
+
+
+def test_no_device_is_reported():
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a device is present: this host-only case would launch")
+    assert _call("spec_verify_bf16") == _lib.SV_ENODEV
+    assert _call("spec_verify_f32") == _lib.SV_ENODEV
