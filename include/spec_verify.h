@@ -68,7 +68,7 @@ typedef enum {
   SV_ENOMEM = -5,   /* workspace allocation failed or caller workspace too small */
 } sv_status;
 
-#define SV_MAX_D 64   /* largest draft length D accepted */
+#define SV_MAX_D 31   /* largest draft length D accepted (positions 0..D fit one 32-bit mask) */
 
 /* bf16 logits (bit patterns of bfloat16, 2 bytes each). Returns SV_OK or a negative sv_status.
  * Uses a library-owned workspace on the current device, allocated on first use and grown
@@ -92,8 +92,10 @@ size_t spec_verify_workspace_bytes(int B, int D, int V);
 
 /* Same operation with caller-provided device workspace of at least
  * spec_verify_workspace_bytes(B, D, V) bytes, 256-byte aligned. dtype: 0 = fp32, 1 = bf16.
- * Nothing is allocated. The workspace must not be used by another call until this call's
- * stream work has completed. */
+ * Nothing is allocated. The workspace must be zero-filled before its first use; every call
+ * leaves the parts later calls rely on zeroed again (when a later call has a larger B, the
+ * library clears the extra counter slots itself, with a small kernel on `stream`). It must not
+ * be used by another call until this call's stream work has completed. */
 int spec_verify_ws(int dtype, const void* target_logits, const void* draft_logits,
                    const int32_t* draft_tokens, const int32_t* draft_lens,
                    const float* uniforms, int B, int D, int V,

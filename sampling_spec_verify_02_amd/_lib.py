@@ -12,7 +12,7 @@ LIB_NAME = "libspecverify.so"
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
 
 SV_OK, SV_EINVAL, SV_EDTYPE, SV_EHIP, SV_ENODEV, SV_ENOMEM = 0, -1, -2, -3, -4, -5
-SV_MAX_D = 64
+SV_MAX_D = 31
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 _p = ctypes.c_void_p

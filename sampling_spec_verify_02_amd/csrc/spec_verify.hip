@@ -1,58 +1,116 @@
-// Speculative-decoding verification sampler for MI355X (gfx950): kernels and C ABI.
+// Speculative-decoding verification sampler for MI355X (gfx950): fused kernel and C ABI.
 //
-// The operation is defined in include/spec_verify.h (accept rule, residual and bonus draws
-// from "Speculative Speculative Decoding - асинхронизируй это", SD recap; bonus token from
-// "Accélérer Sonar par la Spéculation", section "Décodage spéculatif"; in-order acceptance and
-// AL range from "NVIDIA: öt irányelv ...", section "Mit csinál a spekulatív dekódolás?").
+// The operation is the one stated in include/spec_verify.h: accept / reject / residual rule
+// from "Speculative Speculative Decoding - асинхронизируй это" (recap of standard speculative
+// decoding), the bonus token from "Accélérer Sonar par la Spéculation" (section "Décodage
+// spéculatif"), in-order acceptance up to the first mismatch and AL in [1, 1 + D] from
+// "NVIDIA: öt irányelv ..." (section "Mit csinál a spekulatív dekódolás?").
 //
-// Pipeline (all on the caller's stream, no host synchronisation):
-//   1. row_stats      one workgroup per (row, 16K-element chunk): exact max and
-//                     sum exp((x - max)/T) in fp32 (sampled rows) or max and lowest argmax
-//                     (greedy target rows). Streams every needed logit once with 16-byte loads.
-//   2. accept_scan    one wavefront per sequence: merges chunk partials, gathers the logits of
-//                     the draft tokens, runs the first-reject scan, writes AL and the accepted
-//                     tokens, and describes the final draw (residual row j or bonus row L).
-//   3. final_norm     fp64 normalisers of the rows of the final draw, per 8K-element chunk.
-//   4. final_mass     fp64 per-chunk mass of the draw's weights (residual max(0, p - q), or p).
-//   5. final_pick     per sequence: locate the chunk holding u * Z, rescan it with an fp64
-//                     prefix scan and write the drawn token.
-// The final draw is computed in fp64 because a decision that sits closer to a bin edge than
-// ~1e-5 of that bin's width must still agree with an exact computation.
+// One kernel per call, with two kinds of workgroups.
+//
+// * Row workgroups (one-shot, one per 32 KB chunk of a row, position-major order: all position-0
+//   rows of the batch first, then position 1, ...). Each streams its chunk with non-temporal
+//   16-byte loads and produces the chunk's exact max and fp32 sum exp((x - max) / T) (sampled
+//   rows) or max and lowest argmax (greedy target rows); the chunk holding the draft token x_p
+//   also records the logit at x_p. Rows the method does not need (padding, draft rows of greedy
+//   sequences) cost no memory traffic. The workgroup completing the last chunk of a (sequence,
+//   position) pair evaluates that position's test on its own, u_p < min(1, p_p(x_p)/q_p(x_p))
+//   (or x_p == argmax for greedy), and ORs "position p done" and "position p rejects" into the
+//   sequence's 64-bit state word. The outcome is decided once a rejection is preceded by a
+//   complete prefix of evaluated positions, or once positions 0..L are all done without one;
+//   exactly one OR makes that transition, and its workgroup writes the accepted tokens and AL
+//   and queues the sequence's final draw. Most sequences are decided after their first few
+//   positions, long before the streaming of later positions ends.
+// * Worker workgroups (a few per CU, persistent) take final-draw items from the queue. Item
+//   (b, f) evaluates a 2048-element chunk of the final row(s) in fp64 (target and draft row j
+//   after a rejection at j, target row L for the bonus draw): fp64 normalising sums, and the
+//   residual mass linearised around the fp32 estimate rho~ of rho = S_t / S_d (elements whose
+//   ln(e_t / e_d) is clearly above ln rho~ are certainly in the positive part of p - q and
+//   contribute e_t / S_t - e_d / S_d, those clearly below contribute nothing, those inside the
+//   band are summed apart with the range of their x_t - x_d: one value means one exact ratio
+//   class, resolved exactly later). The worker completing a sequence's last item picks the
+//   token: exact normalisers, exact chunk masses, the chunk holding u * Z, and an fp64
+//   prefix-scan rescan of that chunk.
+//
+// Nothing on the row path ever waits for another workgroup. Hand-offs use device-coherent
+// (sc1) atomic stores and loads and relaxed device-scope atomics: a device-scope
+// release/acquire fence would write back and invalidate the XCD's whole L2 on every hand-off.
+// The counters come in two sets used by alternate calls; each call clears the set the next
+// call will use, so no workgroup has to wait for the others to finish.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
-#include <cstring>
+#include <map>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "spec_verify.h"
 
 namespace sv {
 
-constexpr int kThreads = 256;          // workgroup size of the streaming kernels (4 waves)
-constexpr int kRowChunk = 16384;       // elements per row-statistics unit
-constexpr int kFinChunk = 8192;        // elements per final-draw unit
+constexpr int kThreads = 256;                 // workgroup size (4 wavefronts)
+constexpr int kWaves = kThreads / 64;
+constexpr int kRowChunkBytes = 32768;         // bytes of one row per row workgroup
+constexpr int kRowVecs = kRowChunkBytes / 16 / kThreads;   // 16-byte loads per thread (8)
+constexpr int kFinPer = 8;                    // consecutive elements per lane and block
+constexpr int kMinFinChunk = 2048;            // smallest final-draw item (elements)
+constexpr int kMaxFinChunk = 32768;           // largest final-draw item (elements)
+constexpr int kWorkersPerCU = 4;              // final-draw workgroups per CU
 constexpr float kLog2e = 1.4426950408889634f;
+// Half-width of the band (in ln(e_t/e_d)) inside which an element's sign in max(0, p - q) is
+// not decided from the fp32 estimate of ln(S_t/S_d). The fp32 statistics are accurate to a
+// few 1e-6, so the exact ln(S_t/S_d) lies well inside; the pick checks that it does.
+constexpr double kBand = 3e-5;
+constexpr long long kSpinLimit = 4000000;     // polls before a wait gives up
 
 enum Mode : int { kNone = 0, kGreedy = 1, kResidual = 2, kBonus = 3 };
 
-struct RowPart {        // partial statistics of one chunk of one row
-  float m;              // max of the raw logits in the chunk
-  float s;              // sampled rows: sum exp2((x - m) * log2e / T); greedy rows: argmax bits
+struct RowPart {      // partial statistics of one row chunk
+  float m;            // max of the raw logits in the chunk
+  float s;            // sampled rows: sum exp((x - m) / T); greedy rows: bits of the argmax
+  float xv;           // logit at the draft token of this position, if it lies in the chunk
+  float pad;
 };
 
-struct SeqDesc {        // what the final draw of one sequence needs
-  int mode;             // Mode
-  int j;                // position of the final draw
-  float mt, md;         // raw maxima of target row j and draft row j
-  float u;              // final-draw uniform
-  float T;              // temperature
-  int pad0, pad1;
+struct PosInfo {      // what the evaluation of one (sequence, position) found
+  float mt, md;       // exact row maxima (target, draft)
+  float lnrho;        // fp32 ln(S_t / S_d)
+  int g;              // greedy: target argmax
 };
 
-struct FinPart {        // fp64 normalising sums of one chunk of the final-draw rows
-  double st, sd;
+struct SeqDesc {      // what the final draw of one sequence needs
+  int mode;           // Mode
+  int j;              // position of the final draw
+  float mt, md;       // exact maxima of target row j and draft row j
+  float lnrho;        // fp32 estimate of ln(S_t / S_d) for row j (residual only)
+  float u;            // final-draw uniform
+  float T;            // temperature
+  float pad;
+};
+
+struct FinPart {      // fp64 sums of one final-draw chunk
+  double st, sd;      // sum e_t, sum e_d   (e = exp((x - max) / T))
+  double at, ad;      // sums over elements certainly in the positive part of p - q
+  double bt, bd;      // sums over the elements inside the band
+  double dmin, dmax;  // min / max of x_t - x_d inside the band (+inf / -inf: none)
+};
+
+struct Hdr {          // per-call counters of one set
+  unsigned q_seq;     // sequences queued for a final draw
+  unsigned q_items;   // final-draw items published
+  unsigned q_claim;   // final-draw items claimed by workers
+  unsigned decided;   // sequences whose outcome is decided (and queued if sampled)
+  unsigned pad[60];
+};
+
+struct CounterSet {   // everything that must be zero when a call starts
+  Hdr* hdr;
+  unsigned long long* st;   // [B] done bits 0..31, reject bits 32..63
+  unsigned* pc;             // [B][D+1] completed chunks of the position's rows
+  unsigned* fdone;          // [B] completed final-draw items
+  unsigned* qs;             // [B] queue slots: sequence + 1 (0 = not yet written)
 };
 
 struct Params {
@@ -65,67 +123,147 @@ struct Params {
   int32_t* out_len;
   int32_t* out_tokens;
   int B, D, V;
-  int n_row_chunks;
-  int n_fin_chunks;
-  RowPart* row_part;     // [B][2D+1][n_row_chunks]
-  SeqDesc* desc;         // [B]
-  FinPart* fin_part;     // [B][n_fin_chunks]
-  double* fin_mass;      // [B][n_fin_chunks]
-  float* dbg_row_stats;  // optional [B][2D+1][2]
+  int R;              // rows per sequence, 2D + 1 (target 0..D, then draft 0..D-1)
+  int rch;            // elements per row chunk
+  int nchunk;         // row chunks per row
+  int fch;            // elements per final-draw item (multiple of 512)
+  int nF;             // final-draw items per sequence
+  int n_workers;      // worker workgroups (blockIdx < n_workers)
+  CounterSet cur;     // this call's counters
+  CounterSet nxt;     // the next call's counters, cleared by the workers
+  RowPart* rpart;     // [B][R][nchunk]
+  PosInfo* pinfo;     // [B][D+1]
+  SeqDesc* desc;      // [B]
+  FinPart* fpart;     // [B][nF]
+  double* fmass;      // [B][nF] scratch of the pick
+  float* dbg_row_stats;  // optional [B][R][2]
   int32_t* dbg_argmax;   // optional [B][D+1]
   float* dbg_logpq;      // optional [B][D][2]
 };
 
 // ------------------------------------------------------------------------------------------
+// device-coherent accesses
+
+template <typename T>
+__device__ inline void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ inline T ld_dev(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline unsigned add_dev(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline unsigned long long or_dev(unsigned long long* p, unsigned long long v) {
+  return __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wavefront's earlier vector-memory operations (the device-coherent stores of
+// a result) have completed, before a counter announces them.
+__device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ------------------------------------------------------------------------------------------
 // element access
 
 template <typename E> struct Elem;
-template <> struct Elem<uint16_t> {      // bf16 stored as its bit pattern
-  static constexpr int kVec = 8;         // elements per 16-byte load
+template <> struct Elem<uint16_t> {          // bf16 bit patterns
+  static constexpr int kVec = 8;             // elements per 16-byte load
   __device__ static float get(const uint16_t* p, size_t i) {
     return __uint_as_float(uint32_t(p[i]) << 16);
   }
-  __device__ static void unpack(const uint4& v, float* x) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[2 * k] = __uint_as_float(w[k] << 16);
-      x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-    }
+  __device__ static float lane(const uint4& v, int e) {
+    const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
   }
 };
 template <> struct Elem<float> {
   static constexpr int kVec = 4;
   __device__ static float get(const float* p, size_t i) { return p[i]; }
-  __device__ static void unpack(const uint4& v, float* x) {
-    x[0] = __uint_as_float(v.x);
-    x[1] = __uint_as_float(v.y);
-    x[2] = __uint_as_float(v.z);
-    x[3] = __uint_as_float(v.w);
+  __device__ static float lane(const uint4& v, int e) {
+    return __uint_as_float(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
   }
 };
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline uint4 load_stream(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// The run p[a .. a+n), n <= kFinPer, zero past n, kept packed as loaded (16-byte loads when
+// aligned; element loads otherwise, packed the same way).
+template <typename E> struct Run;
+template <> struct Run<uint16_t> {
+  uint32_t w[4];
+  __device__ void load(const uint16_t* p, int a, int n) {
+    const uint16_t* q = p + a;
+    if (n == kFinPer && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
+      const uint4 v = *reinterpret_cast<const uint4*>(q);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t lo = (2 * k < n) ? q[2 * k] : 0u;
+        const uint32_t hi = (2 * k + 1 < n) ? q[2 * k + 1] : 0u;
+        w[k] = lo | (hi << 16);
+      }
+    }
+  }
+  __device__ float at(int e) const {
+    return __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+  }
+};
+template <> struct Run<float> {
+  float x[kFinPer];
+  __device__ void load(const float* p, int a, int n) {
+    const float* q = p + a;
+    if (n == kFinPer && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
+      const float4 v0 = reinterpret_cast<const float4*>(q)[0];
+      const float4 v1 = reinterpret_cast<const float4*>(q)[1];
+      x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+      x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < kFinPer; ++e) x[e] = (e < n) ? q[e] : 0.f;
+    }
+  }
+  __device__ float at(int e) const { return x[e]; }
+};
+
+// wave-uniform values kept in scalar registers
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline double uniform(double v) {
+  const unsigned long long u = __double_as_longlong(v);
+  const unsigned lo = __builtin_amdgcn_readfirstlane(unsigned(u));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(unsigned(u >> 32));
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
 
 __device__ inline bool seq_valid(int L, int D, float T) {
   return L >= 0 && L <= D && isfinite(T) && T >= 0.f;
 }
 
-// Row r of sequence b: r in [0, D] is target position r, r in [D+1, 2D] is draft position
-// r-D-1. Returns nullptr if the row is not needed.
-template <typename E>
-__device__ inline const E* row_ptr(const Params& P, int b, int r, int L, bool greedy) {
-  if (r <= P.D) {
-    if (r > L) return nullptr;
-    return static_cast<const E*>(P.target) + (size_t(b) * (P.D + 1) + r) * size_t(P.V);
-  }
-  const int i = r - P.D - 1;
-  if (greedy || i >= L) return nullptr;
-  return static_cast<const E*>(P.draft) + (size_t(b) * P.D + i) * size_t(P.V);
+// chunks of the rows of (sequence, position p) that the method needs
+__device__ inline int pair_chunks(int p, int L, bool greedy, int nchunk) {
+  return (p <= L ? nchunk : 0) + ((!greedy && p < L) ? nchunk : 0);
+}
+
+// Has the outcome been decided by state word w? Sets j (position of the final token).
+__device__ inline bool decided(unsigned long long w, int L, int& j) {
+  const unsigned done = unsigned(w), rej = unsigned(w >> 32);
+  const int k = __builtin_ctz(~done);                 // positions 0..k-1 evaluated
+  const unsigned pre = (k >= 32) ? 0xffffffffu : ((1u << k) - 1u);
+  const unsigned r = rej & pre;
+  if (r) { j = __builtin_ctz(r); return true; }
+  if (k >= L + 1) { j = L; return true; }
+  return false;
 }
 
 // ------------------------------------------------------------------------------------------
-// reductions
+// reductions (fixed trees, so identical inputs give identical bits)
 
-// (m, s) pairs: s is a sum of exp2((x - m) * k). Empty partials carry s == 0.
+// (m, s) pairs: s is a sum of exp2((x - m) * k); empty partials carry s == 0.
 __device__ inline void ms_combine(float& m, float& s, float m2, float s2, float k) {
   if (s2 == 0.f) return;
   if (s == 0.f) { m = m2; s = s2; return; }
@@ -140,409 +278,679 @@ __device__ inline void am_combine(float& v, int& i, float v2, int i2) {
   if (i < 0 || v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
 
-__device__ inline void block_reduce_ms(float& m, float& s, float k) {
+__device__ inline void wave_ms(float& m, float& s, float k) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     const float m2 = __shfl_xor(m, off);
     const float s2 = __shfl_xor(s, off);
     ms_combine(m, s, m2, s2, k);
   }
-  __shared__ float sm[kThreads / 64], ss[kThreads / 64];
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) { sm[w] = m; ss[w] = s; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int k2 = 1; k2 < kThreads / 64; ++k2) ms_combine(m, s, sm[k2], ss[k2], k);
-  }
 }
 
-__device__ inline void block_reduce_am(float& v, int& i) {
+__device__ inline void wave_am(float& v, int& i) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     const float v2 = __shfl_xor(v, off);
     const int i2 = __shfl_xor(i, off);
     am_combine(v, i, v2, i2);
   }
-  __shared__ float sv[kThreads / 64];
-  __shared__ int si[kThreads / 64];
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) { sv[w] = v; si[w] = i; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int k = 1; k < kThreads / 64; ++k) am_combine(v, i, sv[k], si[k]);
-  }
 }
 
-__device__ inline double block_sum_f64(double x) {
+__device__ inline double wave_sum(double x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  __shared__ double sd[kThreads / 64];
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sd[w] = x;
-  __syncthreads();
-  double t = 0.0;
-  for (int k = 0; k < kThreads / 64; ++k) t += sd[k];
-  return t;   // identical in every thread
+  return x;
+}
+__device__ inline double wave_min(double x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmin(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ inline double wave_max(double x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmax(x, __shfl_xor(x, off));
+  return x;
 }
 
 // ------------------------------------------------------------------------------------------
-// 1. row statistics
+// shared memory of one workgroup
+
+struct Shared {
+  double exp_tab[256];          // 2^(i/256), workers only
+  double red[kWaves][8];
+  int flag;
+};
+
+// fp64 exp: e^t = 2^(k/256) * e^f with k = rint(t * 256 / ln 2) and f = t - k * ln2/256
+// (|f| <= ln2/512; ln2/256 split in two parts so that k * hi is exact), e^f from its degree-4
+// Taylor polynomial (truncation below 4e-17 relative), 2^(k/256) = tab[k mod 256] * 2^(k div 256).
+__device__ inline double exp64(double t, const double* tab) {
+  const double y = t * 369.3299304675746;                  // 256 / ln 2
+  const double kf = __builtin_rint(y);
+  double f = fma(-kf, 0.002707606172407395, t);            // ln2/256, high part
+  f = fma(-kf, 1.6548911585192516e-12, f);                 // ln2/256, low part
+  const int k = int(kf);
+  const double p = fma(fma(fma(fma(f, 1.0 / 24.0, 1.0 / 6.0), f, 0.5), f, 1.0), f, 1.0);
+  return ldexp(tab[k & 255] * p, k >> 8);
+}
+
+// ------------------------------------------------------------------------------------------
+// outcome of a sequence (wavefront 0 of the deciding workgroup)
 
 template <typename E>
-__global__ __launch_bounds__(kThreads) void row_stats_kernel(Params P) {
-  constexpr int kVec = Elem<E>::kVec;
-  constexpr int kPerThread = kRowChunk / kVec / kThreads;   // 16-byte loads per thread
-  const int R = 2 * P.D + 1;
-  const int unit = blockIdx.x;
-  const int c = unit % P.n_row_chunks;
-  const int br = unit / P.n_row_chunks;
-  const int b = br / R, r = br % R;
-  const int L = P.lens ? P.lens[b] : P.D;
+__device__ void decide(const Params& P, int b, int L, float T, bool greedy, int j, int lane) {
+  const int D = P.D;
+  const int32_t* xs = P.tokens + size_t(b) * D;
+  int32_t* toks = P.out_tokens + size_t(b) * (D + 1);
+  const bool bad = lane < L && (xs[lane] < 0 || xs[lane] >= P.V);   // L <= D <= 31
+  if (__any(bad)) {
+    for (int i = lane; i <= D; i += 64) toks[i] = -1;
+    if (lane == 0) {
+      P.out_len[b] = 0;
+      add_dev(&P.cur.hdr->decided, 1u);
+    }
+    return;
+  }
+  if (greedy) {
+    for (int i = lane; i <= D; i += 64)
+      toks[i] = (i <= j) ? ld_dev(&P.pinfo[size_t(b) * (D + 1) + i].g) : -1;
+    if (lane == 0) {
+      P.out_len[b] = j + 1;
+      add_dev(&P.cur.hdr->decided, 1u);
+    }
+    return;
+  }
+  for (int i = lane; i <= D; i += 64) {
+    if (i < j) toks[i] = xs[i];
+    else if (i > j) toks[i] = -1;      // position j is written by the final draw
+  }
+  if (lane == 0) {
+    P.out_len[b] = j + 1;
+    const PosInfo* pi = P.pinfo + size_t(b) * (D + 1) + j;
+    SeqDesc* d = P.desc + b;
+    st_dev(&d->mode, int(j < L ? kResidual : kBonus));
+    st_dev(&d->j, j);
+    st_dev(&d->mt, ld_dev(&pi->mt));
+    st_dev(&d->md, j < L ? ld_dev(&pi->md) : 0.f);
+    st_dev(&d->lnrho, j < L ? ld_dev(&pi->lnrho) : 0.f);
+    st_dev(&d->u, P.uniforms[size_t(b) * (D + 1) + D]);
+    st_dev(&d->T, T);
+    wait_stores();
+    const unsigned slot = add_dev(&P.cur.hdr->q_seq, 1u);
+    st_dev(P.cur.qs + slot, unsigned(b + 1));
+    wait_stores();
+    add_dev(&P.cur.hdr->q_items, unsigned(P.nF));
+    add_dev(&P.cur.hdr->decided, 1u);
+  }
+}
+
+// Evaluation of position p of sequence b once all its chunks are in (whole workgroup calls it;
+// wavefront 0 does the work).
+template <typename E>
+__device__ void evaluate(const Params& P, int b, int p, int L, float T, bool greedy, int tid) {
+  if (tid >= 64) return;
+  const int lane = tid;
+  const int D = P.D, R = P.R, nc = P.nchunk;
+  const RowPart* tpart = P.rpart + (size_t(b) * R + p) * nc;
+  const RowPart* dpart = P.rpart + (size_t(b) * R + D + 1 + p) * nc;
+  PosInfo* pi = P.pinfo + size_t(b) * (D + 1) + p;
+  bool reject = false;
+  if (greedy) {
+    float v = -INFINITY;
+    int idx = -1;
+    for (int c = lane; c < nc; c += 64)
+      am_combine(v, idx, ld_dev(&tpart[c].m), __float_as_int(ld_dev(&tpart[c].s)));
+    wave_am(v, idx);
+    if (p < L) reject = (P.tokens[size_t(b) * D + p] != idx);
+    if (lane == 0) {
+      st_dev(&pi->g, idx);
+      if (P.dbg_argmax) P.dbg_argmax[size_t(b) * (D + 1) + p] = idx;
+    }
+  } else {
+    const float k2 = kLog2e / T;
+    float mt = -INFINITY, stt = 0.f, md = -INFINITY, sd = 0.f;
+    for (int c = lane; c < nc; c += 64) {
+      ms_combine(mt, stt, ld_dev(&tpart[c].m), ld_dev(&tpart[c].s), k2);
+      if (p < L) ms_combine(md, sd, ld_dev(&dpart[c].m), ld_dev(&dpart[c].s), k2);
+    }
+    wave_ms(mt, stt, k2);
+    if (p < L) wave_ms(md, sd, k2);
+    const float lnt = logf(stt), lnd = logf(sd);
+    float lp = NAN, lq = NAN;
+    if (p < L) {
+      const int x = P.tokens[size_t(b) * D + p];
+      if (x >= 0 && x < P.V) {
+        const int cx = x / P.rch;
+        const float xt = ld_dev(&tpart[cx].xv);
+        const float xd = ld_dev(&dpart[cx].xv);
+        lp = (xt - mt) / T - lnt;
+        lq = (xd - md) / T - lnd;
+        const float ratio = expf(lp - lq);
+        reject = !(P.uniforms[size_t(b) * (D + 1) + p] < fminf(1.f, ratio));
+      } else {
+        reject = true;                 // invalid token: the decision marks the row
+      }
+    }
+    if (lane == 0) {
+      st_dev(&pi->mt, mt);
+      st_dev(&pi->md, md);
+      st_dev(&pi->lnrho, lnt - lnd);
+      if (P.dbg_row_stats) {
+        P.dbg_row_stats[(size_t(b) * R + p) * 2] = mt / T;
+        P.dbg_row_stats[(size_t(b) * R + p) * 2 + 1] = lnt;
+        if (p < L) {
+          P.dbg_row_stats[(size_t(b) * R + D + 1 + p) * 2] = md / T;
+          P.dbg_row_stats[(size_t(b) * R + D + 1 + p) * 2 + 1] = lnd;
+        }
+      }
+      if (P.dbg_logpq && p < L) {
+        P.dbg_logpq[(size_t(b) * D + p) * 2] = lp;
+        P.dbg_logpq[(size_t(b) * D + p) * 2 + 1] = lq;
+      }
+    }
+  }
+  unsigned long long old = 0;
+  if (lane == 0) {
+    wait_stores();
+    const unsigned long long bits = (1ull << p) | (reject ? (1ull << (32 + p)) : 0ull);
+    old = or_dev(P.cur.st + b, bits);
+    const unsigned long long now = old | bits;
+    int j0 = 0, j1 = 0;
+    const bool was = decided(old, L, j0);
+    const bool is = decided(now, L, j1);
+    old = (is && !was) ? (unsigned long long)(j1 + 1) : 0ull;
+  }
+  old = __shfl(old, 0);
+  if (old) decide<E>(P, b, L, T, greedy, int(old) - 1, lane);
+}
+
+// ------------------------------------------------------------------------------------------
+// row workgroup
+
+template <typename E>
+__device__ void row_workgroup(const Params& P, Shared& sm, long long rid, int tid) {
+  constexpr int kV = Elem<E>::kVec;
+  const int nc = P.nchunk;
+  const long long per_p = (long long)P.B * 2 * nc;
+  const int p = int(rid / per_p);
+  const long long rem = rid - (long long)p * per_p;
+  const int b = int(rem / (2 * nc));
+  const int which = int(rem % (2 * nc)) / nc;          // 0 target row p, 1 draft row p
+  const int c = int(rem % nc);
+  const int D = P.D;
+  const int L = P.lens ? P.lens[b] : D;
   const float T = P.temperature[b];
-  if (!seq_valid(L, P.D, T)) return;
+
+  if (!seq_valid(L, D, T)) {
+    // invalid length or temperature: one workgroup of the sequence marks the row
+    if (p == 0 && which == 0 && c == 0) {
+      int32_t* toks = P.out_tokens + size_t(b) * (D + 1);
+      for (int i = tid; i <= D; i += kThreads) toks[i] = -1;
+      if (tid == 0) {
+        P.out_len[b] = 0;
+        add_dev(&P.cur.hdr->decided, 1u);
+      }
+    }
+    return;
+  }
   const bool greedy = (T == 0.f);
-  const E* row = row_ptr<E>(P, b, r, L, greedy);
-  if (row == nullptr) return;
+  if (which == 0 ? (p > L) : (greedy || p >= L)) return;   // row not needed
 
-  const size_t c0 = size_t(c) * kRowChunk;
-  const int n = int(min(size_t(kRowChunk), size_t(P.V) - c0));
-  const E* p = row + c0;
-  const bool aligned = (reinterpret_cast<uintptr_t>(p) & 15) == 0;
-  const int nvec = aligned ? n / kVec : 0;
-  const int tid = threadIdx.x;
-  RowPart* out = P.row_part + size_t(br) * P.n_row_chunks + c;
+  const int r = which == 0 ? p : D + 1 + p;
+  const E* row = which == 0
+      ? static_cast<const E*>(P.target) + (size_t(b) * (D + 1) + p) * size_t(P.V)
+      : static_cast<const E*>(P.draft) + (size_t(b) * D + p) * size_t(P.V);
+  const int c0 = c * P.rch;
+  const int n = min(P.rch, P.V - c0);
+  const E* ptr = row + c0;
+  const bool aligned = (reinterpret_cast<uintptr_t>(ptr) & 15) == 0;
+  const int nvec = aligned ? n / kV : 0;
 
-  uint4 buf[kPerThread];
+  uint4 buf[kRowVecs];
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
+  for (int k = 0; k < kRowVecs; ++k) {
     const int vi = tid + k * kThreads;
-    if (vi < nvec) buf[k] = reinterpret_cast<const uint4*>(p)[vi];
+    if (vi < nvec) buf[k] = load_stream(reinterpret_cast<const uint4*>(ptr) + vi);
+  }
+  float xv = 0.f;
+  if (!greedy && tid == 0 && p < L) {
+    const int x = P.tokens[size_t(b) * D + p];
+    if (x >= c0 && x < c0 + n) xv = Elem<E>::get(row, x);
   }
 
+  float m, s;
   if (greedy) {
     float best = -INFINITY;
     int bi = -1;
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
+    for (int k = 0; k < kRowVecs; ++k) {
       const int vi = tid + k * kThreads;
       if (vi < nvec) {
-        float x[kVec];
-        Elem<E>::unpack(buf[k], x);
 #pragma unroll
-        for (int e = 0; e < kVec; ++e)
-          if (bi < 0 || x[e] > best) { best = x[e]; bi = vi * kVec + e; }
+        for (int e = 0; e < kV; ++e) {
+          const float x = Elem<E>::lane(buf[k], e);
+          if (bi < 0 || x > best) { best = x; bi = vi * kV + e; }
+        }
       }
     }
-    for (int i = nvec * kVec + tid; i < n; i += kThreads)
-      am_combine(best, bi, Elem<E>::get(p, i), i);
-    block_reduce_am(best, bi);
-    if (tid == 0) { out->m = best; out->s = __int_as_float(bi < 0 ? -1 : int(c0) + bi); }
-    return;
-  }
-
-  const float k2 = kLog2e / T;
-  float m = -INFINITY;
+    for (int i = nvec * kV + tid; i < n; i += kThreads) am_combine(best, bi, Elem<E>::get(ptr, i), i);
+    wave_am(best, bi);
+    float* rv = reinterpret_cast<float*>(&sm.red[0][0]);
+    int* ri = reinterpret_cast<int*>(&sm.red[0][4]);
+    if ((tid & 63) == 0) { rv[tid >> 6] = best; ri[tid >> 6] = bi; }
+    __syncthreads();
+    if (tid == 0)
+      for (int w = 1; w < kWaves; ++w) am_combine(best, bi, rv[w], ri[w]);
+    m = best;
+    s = __int_as_float(bi < 0 ? -1 : c0 + bi);
+  } else {
+    // online max / sum per 16-byte vector: only one vector's elements are live at a time
+    const float k2 = kLog2e / T;
+    float mx = -INFINITY, sum = 0.f;
 #pragma unroll
-  for (int k = 0; k < kPerThread; ++k) {
-    const int vi = tid + k * kThreads;
-    if (vi < nvec) {
-      float x[kVec];
-      Elem<E>::unpack(buf[k], x);
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) m = fmaxf(m, x[e]);
-    }
-  }
-  for (int i = nvec * kVec + tid; i < n; i += kThreads) m = fmaxf(m, Elem<E>::get(p, i));
-  float s = 0.f;
-  if (m > -INFINITY) {
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
+    for (int k = 0; k < kRowVecs; ++k) {
       const int vi = tid + k * kThreads;
       if (vi < nvec) {
-        float x[kVec];
-        Elem<E>::unpack(buf[k], x);
+        float mk = Elem<E>::lane(buf[k], 0);
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) s += __builtin_amdgcn_exp2f((x[e] - m) * k2);
+        for (int e = 1; e < kV; ++e) mk = fmaxf(mk, Elem<E>::lane(buf[k], e));
+        if (k == 0) {
+          mx = mk;
+        } else {
+          const float mn = fmaxf(mx, mk);
+          sum *= __builtin_amdgcn_exp2f((mx - mn) * k2);
+          mx = mn;
+        }
+        const float off = -mx * k2;
+#pragma unroll
+        for (int e = 0; e < kV; ++e) sum += __builtin_amdgcn_exp2f(fmaf(Elem<E>::lane(buf[k], e), k2, off));
       }
     }
-    for (int i = nvec * kVec + tid; i < n; i += kThreads)
-      s += __builtin_amdgcn_exp2f((Elem<E>::get(p, i) - m) * k2);
-  }
-  block_reduce_ms(m, s, k2);
-  if (tid == 0) { out->m = m; out->s = s; }
-}
-
-// ------------------------------------------------------------------------------------------
-// 2. accept scan: one wavefront per sequence
-
-template <typename E>
-__global__ __launch_bounds__(64) void accept_scan_kernel(Params P) {
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int D = P.D, R = 2 * D + 1;
-  const int L = P.lens ? P.lens[b] : D;
-  const float T = P.temperature[b];
-  int32_t* toks = P.out_tokens + size_t(b) * (D + 1);
-  SeqDesc* desc = P.desc + b;
-
-  bool ok = seq_valid(L, D, T);
-  if (ok) {
-    bool bad = false;
-    for (int i = lane; i < L; i += 64) {
-      const int x = P.tokens[size_t(b) * D + i];
-      bad |= (x < 0 || x >= P.V);
-    }
-    ok = !__any(bad);
-  }
-  if (P.dbg_row_stats)
-    for (int r = lane; r < R; r += 64) {
-      P.dbg_row_stats[(size_t(b) * R + r) * 2] = NAN;
-      P.dbg_row_stats[(size_t(b) * R + r) * 2 + 1] = NAN;
-    }
-  if (P.dbg_argmax)
-    for (int i = lane; i <= D; i += 64) P.dbg_argmax[size_t(b) * (D + 1) + i] = -1;
-  if (P.dbg_logpq)
-    for (int i = lane; i < 2 * D; i += 64) P.dbg_logpq[size_t(b) * D * 2 + i] = NAN;
-  if (!ok) {
-    for (int i = lane; i <= D; i += 64) toks[i] = -1;
-    if (lane == 0) { P.out_len[b] = 0; desc->mode = kNone; }
-    return;
-  }
-  const bool greedy = (T == 0.f);
-
-  __shared__ float s_m[2 * SV_MAX_D + 1];
-  __shared__ float s_lns[2 * SV_MAX_D + 1];
-  __shared__ int s_arg[SV_MAX_D + 1];
-  const float k2 = greedy ? 0.f : kLog2e / T;
-  for (int r = lane; r < R; r += 64) {
-    if (row_ptr<E>(P, b, r, L, greedy) == nullptr) continue;
-    const RowPart* part = P.row_part + (size_t(b) * R + r) * P.n_row_chunks;
-    if (greedy) {
-      float v = -INFINITY;
-      int idx = -1;
-      for (int c = 0; c < P.n_row_chunks; ++c) am_combine(v, idx, part[c].m, __float_as_int(part[c].s));
-      s_arg[r] = idx;
-      if (P.dbg_argmax) P.dbg_argmax[size_t(b) * (D + 1) + r] = idx;
-    } else {
-      float m = -INFINITY, s = 0.f;
-      for (int c = 0; c < P.n_row_chunks; ++c) ms_combine(m, s, part[c].m, part[c].s, k2);
-      s_m[r] = m;
-      s_lns[r] = logf(s);
-      if (P.dbg_row_stats) {
-        P.dbg_row_stats[(size_t(b) * R + r) * 2] = m / T;
-        P.dbg_row_stats[(size_t(b) * R + r) * 2 + 1] = logf(s);
+    for (int i = nvec * kV + tid; i < n; i += kThreads) {
+      const float x = Elem<E>::get(ptr, i);
+      if (x > mx) {
+        sum = (sum == 0.f) ? 0.f : sum * __builtin_amdgcn_exp2f((mx - x) * k2);
+        mx = x;
       }
+      sum += __builtin_amdgcn_exp2f((x - mx) * k2);
     }
+    wave_ms(mx, sum, k2);
+    float* rm = reinterpret_cast<float*>(&sm.red[0][0]);
+    float* rs = reinterpret_cast<float*>(&sm.red[0][4]);
+    if ((tid & 63) == 0) { rm[tid >> 6] = mx; rs[tid >> 6] = sum; }
+    __syncthreads();
+    if (tid == 0)
+      for (int w = 1; w < kWaves; ++w) ms_combine(mx, sum, rm[w], rs[w], k2);
+    m = mx;
+    s = sum;
+  }
+
+  if (tid == 0) {
+    RowPart* out = P.rpart + (size_t(b) * P.R + r) * nc + c;
+    st_dev(&out->m, m);
+    st_dev(&out->s, s);
+    st_dev(&out->xv, xv);
+    wait_stores();
+    const unsigned done = add_dev(P.cur.pc + size_t(b) * (D + 1) + p, 1u) + 1u;
+    sm.flag = (done == unsigned(pair_chunks(p, L, greedy, nc))) ? 1 : 0;
   }
   __syncthreads();
-
-  if (greedy) {
-    if (lane == 0) {
-      int j = 0;
-      while (j < L && P.tokens[size_t(b) * D + j] == s_arg[j]) { toks[j] = s_arg[j]; ++j; }
-      toks[j] = s_arg[j];
-      for (int i = j + 1; i <= D; ++i) toks[i] = -1;
-      P.out_len[b] = j + 1;
-      desc->mode = kGreedy;
-      desc->j = j;
-    }
-    return;
-  }
-
-  // sampled: log-domain ratio per tested position, then first rejection
-  bool reject = false;
-  int x = 0;
-  if (lane < L) {
-    x = P.tokens[size_t(b) * D + lane];
-    const E* trow = static_cast<const E*>(P.target) + (size_t(b) * (D + 1) + lane) * size_t(P.V);
-    const E* drow = static_cast<const E*>(P.draft) + (size_t(b) * D + lane) * size_t(P.V);
-    const float xt = Elem<E>::get(trow, x);
-    const float xd = Elem<E>::get(drow, x);
-    const float lp = (xt - s_m[lane]) / T - s_lns[lane];
-    const float lq = (xd - s_m[D + 1 + lane]) / T - s_lns[D + 1 + lane];
-    const float ratio = expf(lp - lq);
-    const float u = P.uniforms[size_t(b) * (D + 1) + lane];
-    reject = !(u < fminf(1.f, ratio));
-    if (P.dbg_logpq) {
-      P.dbg_logpq[(size_t(b) * D + lane) * 2] = lp;
-      P.dbg_logpq[(size_t(b) * D + lane) * 2 + 1] = lq;
-    }
-  }
-  const unsigned long long rej = __ballot(reject);
-  const int j = rej ? __builtin_ctzll(rej) : L;
-  for (int i = lane; i <= D; i += 64) {
-    if (i < j) toks[i] = P.tokens[size_t(b) * D + i];
-    else toks[i] = -1;
-  }
-  if (lane == 0) {
-    P.out_len[b] = j + 1;
-    desc->mode = (j < L) ? kResidual : kBonus;
-    desc->j = j;
-    desc->mt = s_m[j];
-    desc->md = (j < L) ? s_m[D + 1 + j] : 0.f;
-    desc->u = P.uniforms[size_t(b) * (D + 1) + D];
-    desc->T = T;
-  }
+  if (sm.flag) evaluate<E>(P, b, p, L, T, greedy, tid);
 }
 
 // ------------------------------------------------------------------------------------------
-// 3-5. final draw in fp64
+// final draw (wave-level workers)
+//
+// A final-draw item covers fch consecutive elements (fch a multiple of 512) of the final row(s)
+// of one sequence. Inside an item, block k holds elements [512k, 512k + 512) and lane l of the
+// wavefront handles elements 512k + 8l .. 512k + 8l + 7 of each block (16-byte loads).
+
+struct Draw {           // what the fp64 evaluation of one sequence's final row(s) needs
+  bool residual;
+  int j;
+  double mt, md, invT, lnrho, u;
+};
 
 template <typename E>
-__device__ inline double exp_weight(const E* row, int v, double m, double invT) {
-  return exp((double(Elem<E>::get(row, v)) - m) * invT);
+__device__ inline const E* final_row(const Params& P, int b, int j, bool draft) {
+  return draft ? static_cast<const E*>(P.draft) + (size_t(b) * P.D + j) * size_t(P.V)
+               : static_cast<const E*>(P.target) + (size_t(b) * (P.D + 1) + j) * size_t(P.V);
 }
 
+// Exact weight of element e of the runs: e_t when target_only, else max(0, e_t/S_t - e_d/S_d).
 template <typename E>
-__global__ __launch_bounds__(kThreads) void final_norm_kernel(Params P) {
-  const int b = blockIdx.x / P.n_fin_chunks;
-  const int c = blockIdx.x % P.n_fin_chunks;
-  const SeqDesc d = P.desc[b];
-  if (d.mode != kResidual && d.mode != kBonus) return;
-  const E* trow = static_cast<const E*>(P.target) + (size_t(b) * (P.D + 1) + d.j) * size_t(P.V);
-  const E* drow = static_cast<const E*>(P.draft) + (size_t(b) * P.D + d.j) * size_t(P.V);
-  const double invT = 1.0 / double(d.T);
-  const int v0 = c * kFinChunk, v1 = min(P.V, v0 + kFinChunk);
+__device__ inline double exact_weight(const Run<E>& rt, const Run<E>& rd, int e, const Draw& w,
+                                      bool target_only, double it, double id, const double* tab) {
+  const double et = exp64((double(rt.at(e)) - w.mt) * w.invT, tab);
+  if (target_only) return et;
+  const double ed = exp64((double(rd.at(e)) - w.md) * w.invT, tab);
+  return fmax(0.0, et * it - ed * id);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ inline double wave_inclusive_scan(double x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Sum of the exact weights of one item's elements (fixed order); target_only as above.
+template <typename E>
+__device__ inline double item_exact_mass(const Params& P, const E* trow, const E* drow,
+                                         const Draw& w, int f, bool target_only, double it,
+                                         double id, const double* tab, int lane) {
+  const int a0 = f * P.fch;
+  const int nblk = (min(P.fch, P.V - a0) + 511) / 512;
+  double s = 0.0;
+  for (int k = 0; k < nblk; ++k) {
+    const int a = a0 + 512 * k + 8 * lane;
+    const int n = max(0, min(kFinPer, P.V - a));
+    if (n > 0) {
+      Run<E> rt, rd;
+      rt.load(trow, a, n);
+      if (!target_only) rd.load(drow, a, n);
+#pragma unroll
+      for (int e = 0; e < kFinPer; ++e) {
+        if (e < n) s += exact_weight<E>(rt, rd, e, w, target_only, it, id, tab);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  return wave_sum(s);
+}
+
+// The last final-draw item of a sequence: exact normalisers, item masses, token (one wavefront).
+template <typename E>
+__device__ void wave_pick(const Params& P, const double* tab, int b, const Draw& w, int lane) {
+  const int nF = P.nF;
+  const FinPart* fp = P.fpart + size_t(b) * nF;
+  double* mass = P.fmass + size_t(b) * nF;
+  const E* trow = final_row<E>(P, b, w.j, false);
+  const E* drow = w.residual ? final_row<E>(P, b, w.j, true) : trow;
+
   double st = 0.0, sd = 0.0;
-  for (int v = v0 + threadIdx.x; v < v1; v += kThreads) {
-    st += exp_weight(trow, v, double(d.mt), invT);
-    if (d.mode == kResidual) sd += exp_weight(drow, v, double(d.md), invT);
+  int multi = 0;
+  for (int f = lane; f < nF; f += 64) {
+    st += ld_dev(&fp[f].st);
+    sd += ld_dev(&fp[f].sd);
+    if (ld_dev(&fp[f].dmin) < ld_dev(&fp[f].dmax)) multi = 1;
   }
-  st = block_sum_f64(st);
-  sd = block_sum_f64(sd);
-  if (threadIdx.x == 0) P.fin_part[size_t(b) * P.n_fin_chunks + c] = FinPart{st, sd};
-}
+  st = wave_sum(st);
+  sd = wave_sum(sd);
+  const double it = 1.0 / st, id = 1.0 / sd;
+  // did the band hold the exact ratio, and is every item's in-band set one ratio class?
+  const bool slow = w.residual && (__any(multi) || !(fabs(log(st / sd) - w.lnrho) < kBand));
 
-__device__ inline void final_totals(const Params& P, int b, double& st, double& sd) {
-  st = 0.0;
-  sd = 0.0;
-  const FinPart* fp = P.fin_part + size_t(b) * P.n_fin_chunks;
-  for (int c = 0; c < P.n_fin_chunks; ++c) { st += fp[c].st; sd += fp[c].sd; }
-}
-
-template <typename E>
-__device__ inline double residual_weight(const E* trow, const E* drow, int v, const SeqDesc& d,
-                                         double invT, double it, double id) {
-  const double pt = exp_weight(trow, v, double(d.mt), invT) * it;
-  const double pd = exp_weight(drow, v, double(d.md), invT) * id;
-  return fmax(0.0, pt - pd);
-}
-
-template <typename E>
-__global__ __launch_bounds__(kThreads) void final_mass_kernel(Params P) {
-  const int b = blockIdx.x / P.n_fin_chunks;
-  const int c = blockIdx.x % P.n_fin_chunks;
-  const SeqDesc d = P.desc[b];
-  if (d.mode != kResidual) return;
-  double st, sd;
-  final_totals(P, b, st, sd);
-  const double it = 1.0 / st, id = 1.0 / sd, invT = 1.0 / double(d.T);
-  const E* trow = static_cast<const E*>(P.target) + (size_t(b) * (P.D + 1) + d.j) * size_t(P.V);
-  const E* drow = static_cast<const E*>(P.draft) + (size_t(b) * P.D + d.j) * size_t(P.V);
-  const int v0 = c * kFinChunk, v1 = min(P.V, v0 + kFinChunk);
-  double w = 0.0;
-  for (int v = v0 + threadIdx.x; v < v1; v += kThreads) w += residual_weight(trow, drow, v, d, invT, it, id);
-  w = block_sum_f64(w);
-  if (threadIdx.x == 0) P.fin_mass[size_t(b) * P.n_fin_chunks + c] = w;
-}
-
-template <typename E>
-__global__ __launch_bounds__(kThreads) void final_pick_kernel(Params P) {
-  const int b = blockIdx.x;
-  const SeqDesc d = P.desc[b];
-  if (d.mode != kResidual && d.mode != kBonus) return;
-  const int tid = threadIdx.x;
-  const int nF = P.n_fin_chunks;
-  double st, sd;
-  final_totals(P, b, st, sd);
-  const double it = 1.0 / st, id = 1.0 / sd, invT = 1.0 / double(d.T);
-  const E* trow = static_cast<const E*>(P.target) + (size_t(b) * (P.D + 1) + d.j) * size_t(P.V);
-  const E* drow = static_cast<const E*>(P.draft) + (size_t(b) * P.D + d.j) * size_t(P.V);
-
-  // residual weights, or (bonus, or a residual of zero total mass) the target's exp weights
-  bool residual = (d.mode == kResidual);
-  const double* mass = P.fin_mass + size_t(b) * nF;
-  const FinPart* fp = P.fin_part + size_t(b) * nF;
-  __shared__ int s_chunk;
-  __shared__ int s_last;
-  __shared__ double s_rem;
-  __shared__ int s_residual;
-  if (tid == 0) {
-    double Z = 0.0;
-    if (residual) for (int c = 0; c < nF; ++c) Z += mass[c];
-    if (!(Z > 0.0)) { residual = false; Z = 0.0; for (int c = 0; c < nF; ++c) Z += fp[c].st; }
-    const double t = double(d.u) * Z;
-    double pre = 0.0;
-    int cs = -1, lastpos = -1;
-    double rem = 0.0;
-    for (int c = 0; c < nF; ++c) {
-      const double wc = residual ? mass[c] : fp[c].st;
-      if (wc > 0.0) lastpos = c;
-      if (cs < 0 && pre + wc > t) { cs = c; rem = t - pre; }
-      pre += wc;
+  bool target_only = !w.residual;
+  if (!slow) {
+    for (int f = lane; f < nF; f += 64) {
+      double m;
+      if (target_only) {
+        m = ld_dev(&fp[f].st);
+      } else {
+        m = ld_dev(&fp[f].at) * it - ld_dev(&fp[f].ad) * id;
+        if (ld_dev(&fp[f].dmin) <= ld_dev(&fp[f].dmax))            // one in-band ratio class
+          m += fmax(0.0, ld_dev(&fp[f].bt) * it - ld_dev(&fp[f].bd) * id);
+        m = fmax(0.0, m);
+      }
+      st_dev(mass + f, m);
     }
-    s_last = (cs < 0) ? 1 : 0;
-    s_chunk = (cs < 0) ? lastpos : cs;
-    s_rem = rem;
-    s_residual = residual ? 1 : 0;
+  } else {
+    for (int f = 0; f < nF; ++f) {
+      const double m = item_exact_mass<E>(P, trow, drow, w, f, false, it, id, tab, lane);
+      if (lane == 0) st_dev(mass + f, m);
+    }
   }
-  __syncthreads();
-  residual = s_residual != 0;
-  const int c = s_chunk;
-  if (c < 0) {                          // no positive weight at all (non-finite logits)
-    if (tid == 0) P.out_tokens[size_t(b) * (P.D + 1) + d.j] = -1;
+  wait_stores();
+
+  // inclusive prefix of the item masses (64 at a time); Z is the last prefix
+  auto prefix = [&](bool from_st) {
+    double total = 0.0;
+    for (int base = 0; base < nF; base += 64) {
+      const int f = base + lane;
+      const double v = (f < nF) ? (from_st ? ld_dev(&fp[f].st) : ld_dev(mass + f)) : 0.0;
+      const double inc = wave_inclusive_scan(v, lane) + total;
+      if (f < nF) st_dev(mass + f, inc);
+      total = __shfl(inc, 63);
+    }
+    wait_stores();
+    return total;
+  };
+  double total = prefix(false);
+  if (!(total > 0.0) && !target_only) {
+    target_only = true;                // residual of zero mass (rounding only): draw from p_j
+    total = prefix(true);
+  }
+  const double t = w.u * total;
+
+  // first item whose inclusive prefix exceeds t (else the last item with positive mass)
+  int fstar = nF, flast = -1;
+  for (int base = 0; base < nF; base += 64) {
+    const int f = base + lane;
+    const double inc = (f < nF) ? ld_dev(mass + f) : 0.0;
+    const double prev = (f > 0 && f < nF) ? ld_dev(mass + f - 1) : 0.0;
+    const unsigned long long over = __ballot(f < nF && inc > t);
+    const unsigned long long pos = __ballot(f < nF && inc > prev);
+    if (over && fstar == nF) fstar = base + __builtin_ctzll(over);
+    if (pos) flast = base + 63 - __builtin_clzll(pos);
+  }
+  const bool past_end = (fstar >= nF);
+  if (past_end) fstar = flast;
+  int32_t* out = P.out_tokens + size_t(b) * (P.D + 1) + w.j;
+  if (fstar < 0) {                     // no positive weight at all
+    if (lane == 0) *out = -1;
     return;
   }
-  const double rem = s_rem;
-  const int v0 = c * kFinChunk, v1 = min(P.V, v0 + kFinChunk);
-  const int n = v1 - v0;
-  const int per = (n + kThreads - 1) / kThreads;
-  const int a0 = v0 + tid * per, a1 = min(v1, a0 + per);
-  auto weight = [&](int v) {
-    return residual ? residual_weight(trow, drow, v, d, invT, it, id)
-                    : exp_weight(trow, v, double(d.mt), invT);
-  };
-  double ts = 0.0;
-  int my_last = -1;
-  for (int v = a0; v < a1; ++v) {
-    const double w = weight(v);
-    ts += w;
-    if (w > 0.0) my_last = v;
-  }
-  // exclusive prefix of the per-thread sums (Hillis-Steele in LDS)
-  __shared__ double s_scan[kThreads];
-  __shared__ int s_found;
-  __shared__ int s_lastv[kThreads];
-  s_scan[tid] = ts;
-  s_lastv[tid] = my_last;
-  if (tid == 0) s_found = -1;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const double add = (tid >= off) ? s_scan[tid - off] : 0.0;
-    __syncthreads();
-    s_scan[tid] += add;
-    __syncthreads();
-  }
-  // thread t owns [incl_{t-1}, incl_t): consecutive stored values, so exactly one owner
-  const double pre = (tid > 0) ? s_scan[tid - 1] : 0.0;
-  if (!s_last && ts > 0.0 && pre <= rem && rem < s_scan[tid]) {
-    double acc = pre;
-    int k = my_last;
-    for (int v = a0; v < a1; ++v) {
-      acc += weight(v);
-      if (acc > rem) { k = v; break; }
+  double run = (fstar > 0) ? ld_dev(mass + fstar - 1) : 0.0;
+
+  // rescan the chosen item block by block, in ascending element order
+  const int a0 = fstar * P.fch;
+  const int nblk = (min(P.fch, P.V - a0) + 511) / 512;
+  int found = -1, last_pos = -1;
+  for (int k = 0; k < nblk && found < 0; ++k) {
+    const int a = a0 + 512 * k + 8 * lane;
+    const int n = max(0, min(kFinPer, P.V - a));
+    Run<E> rt, rd;
+    double ls = 0.0;
+    int my_last = -1;
+    if (n > 0) {
+      rt.load(trow, a, n);
+      if (!target_only) rd.load(drow, a, n);
+#pragma unroll
+      for (int e = 0; e < kFinPer; ++e) {
+        if (e < n) {
+          const double wt = exact_weight<E>(rt, rd, e, w, target_only, it, id, tab);
+          ls += wt;
+          if (wt > 0.0) my_last = a + e;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    s_found = k;
+    const double inc = wave_inclusive_scan(ls, lane) + run;
+    const double pre = inc - ls;
+    // lane l owns [prefix before l, prefix through l): consecutive stored values, one owner
+    const double lo = __shfl_up(inc, 1);
+    const double mylo = (lane == 0) ? run : lo;
+    last_pos = max(last_pos, my_last);
+    const bool owner = !past_end && ls > 0.0 && mylo <= t && t < inc;
+    (void)pre;
+    const unsigned long long own = __ballot(owner);
+    if (own) {
+      const int ol = __builtin_ctzll(own);
+      int k2 = -1;
+      if (lane == ol) {
+        double acc = mylo;
+#pragma unroll
+        for (int e = 0; e < kFinPer; ++e) {
+          if (e < n && k2 < 0) {
+            acc += exact_weight<E>(rt, rd, e, w, target_only, it, id, tab);
+            if (acc > t) k2 = a + e;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (k2 < 0) k2 = my_last;
+      }
+      found = __shfl(k2, ol);
+    }
+    run = __shfl(inc, 63);
+  }
+  // rounding put u * Z past the end: the last element with positive weight
+  for (int off = 32; off > 0; off >>= 1) last_pos = max(last_pos, __shfl_xor(last_pos, off));
+  if (lane == 0) *out = (found >= 0) ? found : last_pos;
+}
+
+template <typename E>
+__device__ void wave_fin_item(const Params& P, const double* tab, int b, int f, const Draw& w,
+                              int lane) {
+  const E* trow = final_row<E>(P, b, w.j, false);
+  const E* drow = w.residual ? final_row<E>(P, b, w.j, true) : trow;
+  const int a0 = f * P.fch;
+  const int nblk = (min(P.fch, P.V - a0) + 511) / 512;
+  const double hi = w.lnrho + kBand, lo = w.lnrho - kBand;
+  double st = 0, sd = 0, at = 0, ad = 0, bt = 0, bd = 0, dmin = INFINITY, dmax = -INFINITY;
+  for (int k = 0; k < nblk; ++k) {
+    const int a = a0 + 512 * k + 8 * lane;
+    const int n = max(0, min(kFinPer, P.V - a));
+    if (n <= 0) continue;
+    Run<E> rt, rd;
+    rt.load(trow, a, n);
+    if (w.residual) rd.load(drow, a, n);
+#pragma unroll
+    for (int e = 0; e < kFinPer; ++e) {
+      if (e >= n) continue;
+      const double xt = double(rt.at(e));
+      const double tt = (xt - w.mt) * w.invT;
+      const double et = exp64(tt, tab);
+      st += et;
+      if (w.residual) {
+        const double xd = double(rd.at(e));
+        const double td = (xd - w.md) * w.invT;
+        const double ed = exp64(td, tab);
+        sd += ed;
+        const double l = tt - td;                      // ln(e_t / e_d)
+        if (l > hi) {
+          at += et;
+          ad += ed;
+        } else if (l >= lo) {
+          bt += et;
+          bd += ed;
+          dmin = fmin(dmin, xt - xd);
+          dmax = fmax(dmax, xt - xd);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one element at a time: bounded register use
+    }
+  }
+  st = wave_sum(st);
+  sd = wave_sum(sd);
+  at = wave_sum(at);
+  ad = wave_sum(ad);
+  bt = wave_sum(bt);
+  bd = wave_sum(bd);
+  dmin = wave_min(dmin);
+  dmax = wave_max(dmax);
+  int last = 0;
+  if (lane == 0) {
+    FinPart* out = P.fpart + size_t(b) * P.nF + f;
+    st_dev(&out->st, st);
+    st_dev(&out->sd, sd);
+    st_dev(&out->at, at);
+    st_dev(&out->ad, ad);
+    st_dev(&out->bt, bt);
+    st_dev(&out->bd, bd);
+    st_dev(&out->dmin, dmin);
+    st_dev(&out->dmax, dmax);
+    wait_stores();
+    last = (add_dev(P.cur.fdone + b, 1u) + 1u == unsigned(P.nF)) ? 1 : 0;
+  }
+  last = __shfl(last, 0);
+  if (last) wave_pick<E>(P, tab, b, w, lane);
+}
+
+// One worker wavefront. The final-draw kernel runs after the row kernel, so every item is
+// published when it starts: wavefront gw takes items gw, gw + W, gw + 2W, ... of the queue
+// (W = all worker wavefronts), with no claiming.
+template <typename E>
+__device__ void wave_worker(const Params& P, const double* tab, int gw, int lane) {
+  const unsigned nF = unsigned(P.nF);
+  const unsigned W = unsigned(P.n_workers) * kWaves;
+  const unsigned n_items = uniform(int(ld_dev(&P.cur.hdr->q_items)));
+  int cur_b = -1;
+  Draw w = {};
+  for (unsigned u = unsigned(gw); u < n_items; u += W) {
+    const unsigned slot = u / nF;
+    const int b = uniform(int(ld_dev(P.cur.qs + slot)) - 1);
+    const int f = int(u % nF);
+    if (b < 0) continue;               // cannot happen: every published slot is written
+    if (b != cur_b) {                  // descriptor fields, one per lane, in one round trip
+      const SeqDesc* d = P.desc + b;
+      int iv = 0;
+      float fv = 0.f;
+      if (lane == 0) iv = ld_dev(&d->mode);
+      if (lane == 1) iv = ld_dev(&d->j);
+      if (lane == 2) fv = ld_dev(&d->mt);
+      if (lane == 3) fv = ld_dev(&d->md);
+      if (lane == 4) fv = ld_dev(&d->lnrho);
+      if (lane == 5) fv = ld_dev(&d->u);
+      if (lane == 6) fv = ld_dev(&d->T);
+      w.residual = uniform(__shfl(iv, 0)) == kResidual;
+      w.j = uniform(__shfl(iv, 1));
+      w.mt = uniform(double(__shfl(fv, 2)));
+      w.md = uniform(double(__shfl(fv, 3)));
+      w.lnrho = uniform(double(__shfl(fv, 4)));
+      w.u = uniform(double(__shfl(fv, 5)));
+      w.invT = uniform(1.0 / double(__shfl(fv, 6)));
+      cur_b = b;
+    }
+    wave_fin_item<E>(P, tab, b, f, w, lane);
+  }
+}
+
+template <typename E>
+__device__ void worker(const Params& P, Shared& sm, int wid, int tid) {
+  for (int i = tid; i < 256; i += kThreads) sm.exp_tab[i] = exp2(double(i) / 256.0);
+
+  // clear the counters of the next call (no workgroup of this call touches them)
+  {
+    const long long stride = (long long)P.n_workers * kThreads;
+    const long long me = (long long)wid * kThreads + tid;
+    for (long long i = me; i < P.B; i += stride) {
+      st_dev(P.nxt.st + i, 0ull);
+      st_dev(P.nxt.fdone + i, 0u);
+      st_dev(P.nxt.qs + i, 0u);
+    }
+    const long long npc = (long long)P.B * (P.D + 1);
+    for (long long i = me; i < npc; i += stride) st_dev(P.nxt.pc + i, 0u);
+    if (wid == 0 && tid < 4) st_dev(reinterpret_cast<unsigned*>(P.nxt.hdr) + tid, 0u);
   }
   __syncthreads();
-  if (tid == 0) {
-    int k = s_found;
-    if (k < 0) {                        // rounding put u*Z past the end: last positive weight
-      for (int t2 = kThreads - 1; t2 >= 0 && k < 0; --t2) k = s_lastv[t2];
-    }
-    P.out_tokens[size_t(b) * (P.D + 1) + d.j] = k;
-  }
+  wave_worker<E>(P, sm.exp_tab, wid * kWaves + (tid >> 6), tid & 63);
+}
+
+// ------------------------------------------------------------------------------------------
+// the kernel
+
+// Row kernel: one workgroup per row chunk (its own register budget, so many stay resident).
+template <typename E>
+__global__ __launch_bounds__(kThreads) void row_kernel(Params P) {
+  __shared__ Shared sm;
+  row_workgroup<E>(P, sm, (long long)blockIdx.x, threadIdx.x);
+}
+
+// Final-draw kernel: persistent worker workgroups (four worker wavefronts each).
+template <typename E>
+__global__ __launch_bounds__(kThreads) void final_kernel(Params P) {
+  __shared__ Shared sm;
+  worker<E>(P, sm, int(blockIdx.x), threadIdx.x);
+}
+
+// Clears the counter region (when a workspace meets a new B or D).
+__global__ void clear_kernel(unsigned* p, long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -550,22 +958,53 @@ __global__ __launch_bounds__(kThreads) void final_pick_kernel(Params P) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Workspace: [counter set 0][counter set 1] [row partials][position info][descriptors]
+//            [final-draw partials][pick scratch]. A counter set is [Hdr][st B][pc B(D+1)]
+//            [fdone B][qs B]; both sets must be zero when a workspace is first used.
 struct Layout {
-  int n_row_chunks, n_fin_chunks;
-  size_t off_row, off_desc, off_fin, off_mass, total;
+  int rch, nchunk, nF;
+  size_t set_bytes, off_st, off_pc, off_fdone, off_qs;   // within a counter set
+  size_t off_rpart, off_pinfo, off_desc, off_fpart, off_fmass, total;
 };
 
-inline bool make_layout(int B, int D, int V, Layout& L) {
+inline bool make_layout(int B, int D, int V, int elem_bytes, Layout& L) {
   if (B <= 0 || D < 0 || V <= 0 || D > SV_MAX_D) return false;
-  L.n_row_chunks = (V + kRowChunk - 1) / kRowChunk;
-  L.n_fin_chunks = (V + kFinChunk - 1) / kFinChunk;
+  L.rch = kRowChunkBytes / elem_bytes;
+  L.nchunk = int((size_t(V) + L.rch - 1) / L.rch);
+  L.nF = int((size_t(V) + kMinFinChunk - 1) / kMinFinChunk);   // most items a row can need
+  size_t o = align256(sizeof(Hdr));
+  L.off_st = o;    o += align256(size_t(B) * 8);
+  L.off_pc = o;    o += align256(size_t(B) * (D + 1) * 4);
+  L.off_fdone = o; o += align256(size_t(B) * 4);
+  L.off_qs = o;    o += align256(size_t(B) * 4);
+  L.set_bytes = o;
+  o = 2 * L.set_bytes;
   const size_t R = size_t(2) * D + 1;
-  L.off_row = 0;
-  L.off_desc = align256(size_t(B) * R * L.n_row_chunks * sizeof(RowPart));
-  L.off_fin = L.off_desc + align256(size_t(B) * sizeof(SeqDesc));
-  L.off_mass = L.off_fin + align256(size_t(B) * L.n_fin_chunks * sizeof(FinPart));
-  L.total = L.off_mass + align256(size_t(B) * L.n_fin_chunks * sizeof(double));
+  L.off_rpart = o; o += align256(size_t(B) * R * L.nchunk * sizeof(RowPart));
+  L.off_pinfo = o; o += align256(size_t(B) * (D + 1) * sizeof(PosInfo));
+  L.off_desc = o;  o += align256(size_t(B) * sizeof(SeqDesc));
+  L.off_fpart = o; o += align256(size_t(B) * L.nF * sizeof(FinPart));
+  L.off_fmass = o; o += align256(size_t(B) * L.nF * sizeof(double));
+  L.total = o;
   return true;
+}
+
+// Workspace bytes: the larger of the two dtypes' layouts, so one size serves both.
+inline size_t workspace_bytes(int B, int D, int V) {
+  Layout a, b;
+  if (!make_layout(B, D, V, 2, a) || !make_layout(B, D, V, 4, b)) return 0;
+  return a.total > b.total ? a.total : b.total;
+}
+
+inline CounterSet counter_set(char* base, const Layout& L, int k) {
+  char* s = base + size_t(k) * L.set_bytes;
+  CounterSet c;
+  c.hdr = reinterpret_cast<Hdr*>(s);
+  c.st = reinterpret_cast<unsigned long long*>(s + L.off_st);
+  c.pc = reinterpret_cast<unsigned*>(s + L.off_pc);
+  c.fdone = reinterpret_cast<unsigned*>(s + L.off_fdone);
+  c.qs = reinterpret_cast<unsigned*>(s + L.off_qs);
+  return c;
 }
 
 struct DeviceWorkspace {
@@ -573,12 +1012,16 @@ struct DeviceWorkspace {
   size_t bytes = 0;
 };
 
-std::mutex g_ws_mutex;
-std::vector<DeviceWorkspace> g_ws;
+struct WsState {      // host-side knowledge about one workspace
+  long long calls = 0;        // calls made with it (the parity picks the counter set)
+  int B = -1, D = -1;         // counter layout of the last call (-1: zero-filled, unused)
+};
 
-// Optional timing of the row-statistics kernel: when armed, each call records one event pair
-// around that kernel on the caller's stream.
-struct Profile {
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, DeviceWorkspace> g_ws;   // library buffers per stream
+std::map<void*, WsState> g_ws_state;
+
+struct Profile {        // optional timing of the kernel: one event pair per call
   std::vector<hipEvent_t> begin, end;
   int used = 0;
   bool armed = false;
@@ -586,22 +1029,49 @@ struct Profile {
 std::mutex g_prof_mutex;
 Profile g_prof;
 
+std::mutex g_dev_mutex;
+std::map<int, int> g_cus;        // device -> compute units
+
 int check_args(const void* t, const void* d, const int32_t* tok, const float* u, const float* temp,
                int32_t* ol, int32_t* ot, int B, int D, int V) {
   if (B <= 0 || D < 0 || V <= 0 || D > SV_MAX_D) return SV_EINVAL;
   if (!t || !u || !temp || !ol || !ot) return SV_EINVAL;
   if (D > 0 && (!d || !tok)) return SV_EINVAL;
-  // element counts must fit comfortably in 64-bit byte offsets
   const unsigned __int128 n = (unsigned __int128)B * (unsigned __int128)(D + 1) * (unsigned __int128)V;
   if (n > ((unsigned __int128)1 << 60)) return SV_EINVAL;
   return SV_OK;
 }
 
+int compute_units(int dev) {
+  std::lock_guard<std::mutex> lk(g_dev_mutex);
+  auto it = g_cus.find(dev);
+  if (it != g_cus.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return -1;
+  g_cus[dev] = cus;
+  return cus;
+}
+
 template <typename E>
-int launch_all(Params& P, hipStream_t stream) {
-  const int R = 2 * P.D + 1;
-  const size_t n_units = size_t(P.B) * R * P.n_row_chunks;
-  if (n_units > 0x7fffffffull) return SV_EINVAL;
+int launch(Params& P, int dev, hipStream_t stream) {
+  const int cus = compute_units(dev);
+  if (cus <= 0) return SV_EHIP;
+  // Worker wavefronts: four per workgroup, kWorkersPerCU workgroups per CU. Items are sized so
+  // each worker wavefront gets about four: small items keep the work after the last decision
+  // short, large ones keep the per-item overhead low when there are many draws.
+  const long long waves = 4ll * kWorkersPerCU * cus;
+  long long fch = ((long long)P.B * P.V + 4 * waves - 1) / (4 * waves);
+  fch = (fch + 511) / 512 * 512;
+  fch = fch < kMinFinChunk ? kMinFinChunk : (fch > kMaxFinChunk ? kMaxFinChunk : fch);
+  P.fch = int(fch);
+  P.nF = int((P.V + fch - 1) / fch);
+  const long long items = (long long)P.B * P.nF;
+  const long long wg = (items + 3) / 4;
+  P.n_workers = int(wg < (long long)kWorkersPerCU * cus ? wg : (long long)kWorkersPerCU * cus);
+  const long long rows = (long long)(P.D + 1) * P.B * 2 * P.nchunk;
+  if (rows > 0x7fffffffll) return SV_EINVAL;
+
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   {
     std::lock_guard<std::mutex> g(g_prof_mutex);
@@ -612,14 +1082,12 @@ int launch_all(Params& P, hipStream_t stream) {
     }
   }
   if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return SV_EHIP;
-  hipLaunchKernelGGL(row_stats_kernel<E>, dim3(unsigned(n_units)), dim3(kThreads), 0, stream, P);
+  hipLaunchKernelGGL(row_kernel<E>, dim3(unsigned(rows)), dim3(kThreads), 0, stream, P);
+  if (hipGetLastError() != hipSuccess) return SV_EHIP;
   if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return SV_EHIP;
-  hipLaunchKernelGGL(accept_scan_kernel<E>, dim3(P.B), dim3(64), 0, stream, P);
-  const unsigned n_fin = unsigned(size_t(P.B) * P.n_fin_chunks);
-  hipLaunchKernelGGL(final_norm_kernel<E>, dim3(n_fin), dim3(kThreads), 0, stream, P);
-  hipLaunchKernelGGL(final_mass_kernel<E>, dim3(n_fin), dim3(kThreads), 0, stream, P);
-  hipLaunchKernelGGL(final_pick_kernel<E>, dim3(P.B), dim3(kThreads), 0, stream, P);
-  return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+  hipLaunchKernelGGL(final_kernel<E>, dim3(unsigned(P.n_workers)), dim3(kThreads), 0, stream, P);
+  if (hipGetLastError() != hipSuccess) return SV_EHIP;
+  return SV_OK;
 }
 
 int run(int dtype, const void* target, const void* draft, const int32_t* tokens,
@@ -630,34 +1098,48 @@ int run(int dtype, const void* target, const void* draft, const int32_t* tokens,
   int rc = check_args(target, draft, tokens, uniforms, temperature, out_len, out_tokens, B, D, V);
   if (rc != SV_OK) return rc;
   Layout lay;
-  make_layout(B, D, V, lay);
+  make_layout(B, D, V, dtype == 1 ? 2 : 4, lay);
+  const size_t need = workspace_bytes(B, D, V);
+  if (ws != nullptr && (ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255)))
+    return SV_ENOMEM;
 
-  std::unique_lock<std::mutex> lock(g_ws_mutex, std::defer_lock);
+  int dev = 0, count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return SV_ENODEV;
+  if (hipGetDevice(&dev) != hipSuccess) return SV_ENODEV;
+
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
   if (ws == nullptr) {
-    int dev = 0, count = 0;
-    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return SV_ENODEV;
-    if (hipGetDevice(&dev) != hipSuccess) return SV_ENODEV;
-    lock.lock();
-    if (g_ws.size() <= size_t(dev)) g_ws.resize(size_t(dev) + 1);
-    DeviceWorkspace& w = g_ws[size_t(dev)];
-    if (w.bytes < lay.total) {
+    DeviceWorkspace& w = g_ws[{dev, stream}];
+    if (w.bytes < need) {
       if (w.ptr) {
-        // the old buffer may still be in use by enqueued work on any stream
-        if (hipDeviceSynchronize() != hipSuccess) return SV_EHIP;
+        // earlier calls on this stream may still use the old buffer
+        if (hipStreamSynchronize(stream) != hipSuccess) return SV_EHIP;
         (void)hipFree(w.ptr);
+        g_ws_state.erase(w.ptr);
         w.ptr = nullptr;
         w.bytes = 0;
       }
-      if (hipMalloc(&w.ptr, lay.total) != hipSuccess) return SV_ENOMEM;
-      w.bytes = lay.total;
+      if (hipMalloc(&w.ptr, need) != hipSuccess) { w.ptr = nullptr; return SV_ENOMEM; }
+      if (hipMemset(w.ptr, 0, need) != hipSuccess) return SV_EHIP;   // counters start at zero
+      w.bytes = need;
     }
     ws = w.ptr;
-    ws_bytes = w.bytes;
-  } else {
-    if (ws_bytes < lay.total || (reinterpret_cast<uintptr_t>(ws) & 255)) return SV_ENOMEM;
   }
+  WsState& state = g_ws_state[ws];
+  char* base = static_cast<char*>(ws);
+  if (state.B >= 0 && (state.B != B || state.D != D)) {
+    // the counter layout changed: clear both counter sets (a small kernel, graph-safe)
+    const long long n = (long long)(2 * lay.set_bytes / 4);
+    hipLaunchKernelGGL(clear_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream,
+                       reinterpret_cast<unsigned*>(base), n);
+    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+  }
+  state.B = B;
+  state.D = D;
+  const int parity = int(state.calls & 1);
+  ++state.calls;
 
-  Params P;
+  Params P = {};
   P.target = target;
   P.draft = draft;
   P.tokens = tokens;
@@ -669,17 +1151,26 @@ int run(int dtype, const void* target, const void* draft, const int32_t* tokens,
   P.B = B;
   P.D = D;
   P.V = V;
-  P.n_row_chunks = lay.n_row_chunks;
-  P.n_fin_chunks = lay.n_fin_chunks;
-  char* base = static_cast<char*>(ws);
-  P.row_part = reinterpret_cast<RowPart*>(base + lay.off_row);
+  P.R = 2 * D + 1;
+  P.rch = lay.rch;
+  P.nchunk = lay.nchunk;
+  P.cur = counter_set(base, lay, parity);
+  P.nxt = counter_set(base, lay, 1 - parity);
+  P.rpart = reinterpret_cast<RowPart*>(base + lay.off_rpart);
+  P.pinfo = reinterpret_cast<PosInfo*>(base + lay.off_pinfo);
   P.desc = reinterpret_cast<SeqDesc*>(base + lay.off_desc);
-  P.fin_part = reinterpret_cast<FinPart*>(base + lay.off_fin);
-  P.fin_mass = reinterpret_cast<double*>(base + lay.off_mass);
+  P.fpart = reinterpret_cast<FinPart*>(base + lay.off_fpart);
+  P.fmass = reinterpret_cast<double*>(base + lay.off_fmass);
   P.dbg_row_stats = dbg_stats;
   P.dbg_argmax = dbg_argmax;
   P.dbg_logpq = dbg_logpq;
-  return dtype == 1 ? launch_all<uint16_t>(P, stream) : launch_all<float>(P, stream);
+  if (dbg_stats && hipMemsetAsync(dbg_stats, 0xff, size_t(B) * P.R * 2 * 4, stream) != hipSuccess)
+    return SV_EHIP;                    // 0xffffffff: NaN for rows that are never evaluated
+  if (dbg_argmax && hipMemsetAsync(dbg_argmax, 0xff, size_t(B) * (D + 1) * 4, stream) != hipSuccess)
+    return SV_EHIP;                    // -1
+  if (dbg_logpq && D > 0 && hipMemsetAsync(dbg_logpq, 0xff, size_t(B) * D * 2 * 4, stream) != hipSuccess)
+    return SV_EHIP;
+  return dtype == 1 ? launch<uint16_t>(P, dev, stream) : launch<float>(P, dev, stream);
 }
 
 }  // namespace sv
@@ -704,10 +1195,7 @@ int spec_verify_f32(const void* target_logits, const void* draft_logits,
                  stream);
 }
 
-size_t spec_verify_workspace_bytes(int B, int D, int V) {
-  sv::Layout lay;
-  return sv::make_layout(B, D, V, lay) ? lay.total : 0;
-}
+size_t spec_verify_workspace_bytes(int B, int D, int V) { return sv::workspace_bytes(B, D, V); }
 
 int spec_verify_ws(int dtype, const void* target_logits, const void* draft_logits,
                    const int32_t* draft_tokens, const int32_t* draft_lens,
@@ -742,7 +1230,7 @@ const char* spec_verify_strerror(int code) {
   }
 }
 
-int spec_verify_version(void) { return 100; }
+int spec_verify_version(void) { return 300; }
 
 int spec_verify_profile_start(int max_calls) {
   if (max_calls <= 0 || max_calls > (1 << 20)) return SV_EINVAL;

@@ -156,7 +156,7 @@ def test_invalid_rows_marked_on_gpu():
 def test_caller_workspace_matches_library_workspace():
     import sampling_spec_verify_02_amd as sv
     w = make("c5", 11, B=96)
-    ws = torch.empty(sv.workspace_bytes(w.B, w.D, w.V), dtype=torch.uint8, device="cuda:0")
+    ws = torch.zeros(sv.workspace_bytes(w.B, w.D, w.V), dtype=torch.uint8, device="cuda:0")
     a = G.run(w)
     b = G.run(w, workspace=ws)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
@@ -192,3 +192,16 @@ def test_lossless_chi_square_on_gpu():
     ok = ~ref.flagged
     assert np.array_equal(al[:k][ok], ref.accept_len[ok])
     assert np.array_equal(out[:k][ok], ref.tokens[ok])
+
+
+def test_workspace_reuse_across_batch_sizes():
+    """The per-sequence counters live at fixed offsets: a workspace used for a small batch and
+    then a larger one must still give exact results (the library clears the new slots)."""
+    import sampling_spec_verify_02_amd as sv
+    ws = torch.zeros(sv.workspace_bytes(300, 7, 129280), dtype=torch.uint8, device="cuda:0")
+    for B, seed in ((40, 1), (300, 2), (17, 3), (300, 4)):
+        w = make("c5", 20 + seed, B=B)
+        ref = verify_workload(w)
+        for wsp in (None, ws):
+            al, toks = G.run(w, workspace=wsp)
+            G.compare(ref, al, toks, f"B={B} caller_ws={wsp is not None}")
