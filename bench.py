@@ -112,6 +112,9 @@ def main():
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain device-to-device copies of 256 MiB (the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (sequences shard over B with no "
@@ -124,6 +127,16 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        nbytes = 256 << 20
+        src = [torch.ones(nbytes // 4, dtype=torch.float32, device=dev) for _ in range(3)]
+        dst = [torch.empty_like(x) for x in src]
+        for k in range(args.steps):
+            dst[k % 3].copy_(src[k % 3])
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": nbytes, "copy_calibration_bytes_written":
+                          nbytes, "copies": args.steps}), flush=True)
+        return
     log(f"bench: generating {args.config} seed {args.seed}")
     w = make(args.config, args.seed)
     alg_bytes, rows = valid_row_bytes(w)

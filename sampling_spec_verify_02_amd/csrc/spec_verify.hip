@@ -57,7 +57,8 @@ constexpr int kRowVecs = kRowChunkBytes / 16 / kThreads;   // 16-byte loads per 
 constexpr int kFinPer = 8;                    // consecutive elements per lane and block
 constexpr int kMinFinChunk = 2048;            // smallest final-draw item (elements)
 constexpr int kMaxFinChunk = 32768;           // largest final-draw item (elements)
-constexpr int kWorkersPerCU = 4;              // final-draw workgroups per CU
+constexpr bool kConcurrent = false;           // final-draw kernel alongside the row kernel
+constexpr int kWorkersPerCU = kConcurrent ? 1 : 4;   // final-draw workgroups per CU
 constexpr float kLog2e = 1.4426950408889634f;
 // Half-width of the band (in ln(e_t/e_d)) inside which an element's sign in max(0, p - q) is
 // not decided from the fp32 estimate of ln(S_t/S_d). The fp32 statistics are accurate to a
@@ -870,21 +871,38 @@ __device__ void wave_fin_item(const Params& P, const double* tab, int b, int f, 
   if (last) wave_pick<E>(P, tab, b, w, lane);
 }
 
-// One worker wavefront. The final-draw kernel runs after the row kernel, so every item is
-// published when it starts: wavefront gw takes items gw, gw + W, gw + 2W, ... of the queue
-// (W = all worker wavefronts), with no claiming.
+// One worker wavefront. Wavefront gw owns the queue items gw, gw + W, gw + 2W, ... (W = all
+// worker wavefronts) and takes them in that order, waiting for each to be published when the
+// final-draw kernel runs alongside the row kernel. It stops at the first owned item that can
+// no longer appear (every sequence decided and the item beyond the last published one).
 template <typename E>
 __device__ void wave_worker(const Params& P, const double* tab, int gw, int lane) {
   const unsigned nF = unsigned(P.nF);
   const unsigned W = unsigned(P.n_workers) * kWaves;
-  const unsigned n_items = uniform(int(ld_dev(&P.cur.hdr->q_items)));
   int cur_b = -1;
   Draw w = {};
-  for (unsigned u = unsigned(gw); u < n_items; u += W) {
-    const unsigned slot = u / nF;
-    const int b = uniform(int(ld_dev(P.cur.qs + slot)) - 1);
+  for (unsigned u = unsigned(gw);; u += W) {
+    int b = -1;
+    if (lane == 0) {
+      long long spins = 0;
+      bool go = false;
+      for (;;) {
+        if (u < ld_dev(&P.cur.hdr->q_items)) { go = true; break; }
+        if (ld_dev(&P.cur.hdr->decided) >= unsigned(P.B) && u >= ld_dev(&P.cur.hdr->q_items)) break;
+        if (++spins > kSpinLimit) break;               // never expected: give up, do not hang
+        __builtin_amdgcn_s_sleep(8);
+      }
+      if (go) {
+        const unsigned slot = u / nF;
+        unsigned q = 0;
+        for (spins = 0; (q = ld_dev(P.cur.qs + slot)) == 0u && spins < kSpinLimit; ++spins)
+          __builtin_amdgcn_s_sleep(1);
+        b = int(q) - 1;
+      }
+    }
+    b = uniform(__shfl(b, 0));
+    if (b < 0) break;
     const int f = int(u % nF);
-    if (b < 0) continue;               // cannot happen: every published slot is written
     if (b != cur_b) {                  // descriptor fields, one per lane, in one round trip
       const SeqDesc* d = P.desc + b;
       int iv = 0;
@@ -1032,6 +1050,29 @@ Profile g_prof;
 std::mutex g_dev_mutex;
 std::map<int, int> g_cus;        // device -> compute units
 
+// A second stream per (device, caller stream) for the final-draw workers, with the two events
+// that fork it from and join it back to the caller's stream. Default priority.
+struct Side {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mutex;
+std::map<std::pair<int, hipStream_t>, Side> g_side;
+
+Side* side_stream(hipStream_t caller) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lk(g_side_mutex);
+  Side& sd = g_side[{dev, caller}];
+  if (!sd.s) {
+    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess) { sd.s = nullptr; return nullptr; }
+    if (hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess)
+      return nullptr;
+  }
+  return &sd;
+}
+
 int check_args(const void* t, const void* d, const int32_t* tok, const float* u, const float* temp,
                int32_t* ol, int32_t* ot, int B, int D, int V) {
   if (B <= 0 || D < 0 || V <= 0 || D > SV_MAX_D) return SV_EINVAL;
@@ -1080,6 +1121,23 @@ int launch(Params& P, int dev, hipStream_t stream) {
       ev1 = g_prof.end[size_t(g_prof.used)];
       ++g_prof.used;
     }
+  }
+  if (kConcurrent) {
+    // the final-draw workers run alongside the row kernel on a second stream: fork after the
+    // caller's earlier work, join before the caller's later work
+    Side* side = side_stream(stream);
+    if (!side) return SV_EHIP;
+    if (hipEventRecord(side->fork, stream) != hipSuccess) return SV_EHIP;
+    if (hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess) return SV_EHIP;
+    hipLaunchKernelGGL(final_kernel<E>, dim3(unsigned(P.n_workers)), dim3(kThreads), 0, side->s, P);
+    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return SV_EHIP;
+    hipLaunchKernelGGL(row_kernel<E>, dim3(unsigned(rows)), dim3(kThreads), 0, stream, P);
+    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return SV_EHIP;
+    if (hipEventRecord(side->join, side->s) != hipSuccess) return SV_EHIP;
+    if (hipStreamWaitEvent(stream, side->join, 0) != hipSuccess) return SV_EHIP;
+    return SV_OK;
   }
   if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return SV_EHIP;
   hipLaunchKernelGGL(row_kernel<E>, dim3(unsigned(rows)), dim3(kThreads), 0, stream, P);
