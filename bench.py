@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "verified rows/s + HBM GB/s (% of peak), B=64 D=7 V=128256 bf16"
 HBM_PEAK_GBPS = 8000.0
 SRC = os.path.join(ROOT, "sampling_spec_verify_02_amd", "csrc", "spec_verify.hip")
-TRAFFIC = os.path.join(ROOT, "profiles", "traffic_row_stats_c3.json")
+TRAFFIC = os.path.join(ROOT, "profiles", "traffic_row_kernel_c3.json")
 
 WORKLOADS = {
     "c1": "B=1 D=4 V=1024 fp32 T=1, N(0,2^2) target, draft +N(0,0.5^2)",
