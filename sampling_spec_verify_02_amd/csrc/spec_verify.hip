@@ -1,4 +1,4 @@
-// Speculative-decoding verification sampler for MI355X (gfx950): fused kernel and C ABI.
+// Speculative-decoding verification sampler for MI355X (gfx950): kernels and C ABI.
 //
 // The operation is the one stated in include/spec_verify.h: accept / reject / residual rule
 // from "Speculative Speculative Decoding - асинхронизируй это" (recap of standard speculative
@@ -6,37 +6,35 @@
 // spéculatif"), in-order acceptance up to the first mismatch and AL in [1, 1 + D] from
 // "NVIDIA: öt irányelv ..." (section "Mit csinál a spekulatív dekódolás?").
 //
-// One kernel per call, with two kinds of workgroups.
+// Three kernels per call, in stream order.
 //
-// * Row workgroups (one-shot, one per 32 KB chunk of a row, position-major order: all position-0
-//   rows of the batch first, then position 1, ...). Each streams its chunk with non-temporal
+// * Row kernel: one workgroup per 32 KB chunk of a row, position-major order (all position-0
+//   rows of the batch first, then position 1, ...). It streams its chunk with non-temporal
 //   16-byte loads and produces the chunk's exact max and fp32 sum exp((x - max) / T) (sampled
 //   rows) or max and lowest argmax (greedy target rows); the chunk holding the draft token x_p
 //   also records the logit at x_p. Rows the method does not need (padding, draft rows of greedy
-//   sequences) cost no memory traffic. The workgroup completing the last chunk of a (sequence,
-//   position) pair evaluates that position's test on its own, u_p < min(1, p_p(x_p)/q_p(x_p))
-//   (or x_p == argmax for greedy), and ORs "position p done" and "position p rejects" into the
-//   sequence's 64-bit state word. The outcome is decided once a rejection is preceded by a
-//   complete prefix of evaluated positions, or once positions 0..L are all done without one;
-//   exactly one OR makes that transition, and its workgroup writes the accepted tokens and AL
-//   and queues the sequence's final draw. Most sequences are decided after their first few
-//   positions, long before the streaming of later positions ends.
-// * Worker workgroups (a few per CU, persistent) take final-draw items from the queue. Item
-//   (b, f) evaluates a 2048-element chunk of the final row(s) in fp64 (target and draft row j
-//   after a rejection at j, target row L for the bonus draw): fp64 normalising sums, and the
-//   residual mass linearised around the fp32 estimate rho~ of rho = S_t / S_d (elements whose
-//   ln(e_t / e_d) is clearly above ln rho~ are certainly in the positive part of p - q and
-//   contribute e_t / S_t - e_d / S_d, those clearly below contribute nothing, those inside the
-//   band are summed apart with the range of their x_t - x_d: one value means one exact ratio
-//   class, resolved exactly later). The worker completing a sequence's last item picks the
-//   token: exact normalisers, exact chunk masses, the chunk holding u * Z, and an fp64
-//   prefix-scan rescan of that chunk.
+//   sequences) are not read. The workgroup completing the last chunk of a (sequence, position)
+//   pair evaluates that position's test, u_p < min(1, p_p(x_p)/q_p(x_p)) (or x_p == argmax for
+//   greedy), and ORs "position p done" and "position p rejects" into the sequence's 64-bit
+//   state word. The outcome is decided once a rejection is preceded by a complete prefix of
+//   evaluated positions, or once positions 0..L are all done without one; exactly one OR makes
+//   that transition, and its wavefront writes the accepted tokens and AL and publishes the
+//   sequence's final-draw descriptor. No workgroup ever waits for another.
+// * Item kernel: one wavefront per final-draw item (b, f), kItemElems consecutive elements of
+//   sequence b's final row(s) (target and draft row j after a rejection at j, target row L for
+//   the bonus draw). It forms fp64 normalising sums and the residual mass linearised around the
+//   fp32 estimate rho~ of rho = S_t / S_d: elements whose x_t - x_d puts ln(e_t / e_d) clearly
+//   above ln rho~ are certainly in the positive part of p - q and contribute e_t / S_t - e_d /
+//   S_d, those clearly below contribute nothing, those inside the band are summed apart with
+//   the range of their x_t - x_d (one value means one exact ratio class, resolved exactly by
+//   the pick).
+// * Pick kernel: one wavefront per sequence. Exact normalisers from the item sums, the item
+//   masses, the item holding u * Z, and an fp64 prefix-scan rescan of that item give the token.
+//   It also clears the counters of the next call.
 //
-// Nothing on the row path ever waits for another workgroup. Hand-offs use device-coherent
-// (sc1) atomic stores and loads and relaxed device-scope atomics: a device-scope
-// release/acquire fence would write back and invalidate the XCD's whole L2 on every hand-off.
-// The counters come in two sets used by alternate calls; each call clears the set the next
-// call will use, so no workgroup has to wait for the others to finish.
+// Hand-offs inside the row kernel use device-coherent (sc1) atomic stores and loads and relaxed
+// device-scope atomics: a device-scope release/acquire fence would write back and invalidate
+// the XCD's whole L2 on every hand-off. The counters come in two sets used by alternate calls.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -55,18 +53,16 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kRowChunkBytes = 32768;         // bytes of one row per row workgroup
 constexpr int kRowVecs = kRowChunkBytes / 16 / kThreads;   // 16-byte loads per thread (8)
 constexpr int kFinPer = 8;                    // consecutive elements per lane and block
-constexpr int kMinFinChunk = 2048;            // smallest final-draw item (elements)
-constexpr int kMaxFinChunk = 32768;           // largest final-draw item (elements)
-constexpr bool kConcurrent = false;           // final-draw kernel alongside the row kernel
-constexpr int kWorkersPerCU = kConcurrent ? 1 : 4;   // final-draw workgroups per CU
+constexpr int kFinBlock = 64 * kFinPer;       // elements per wavefront block (512)
+constexpr int kItemsPerChunk = 8;             // final-draw items per row chunk length
 constexpr float kLog2e = 1.4426950408889634f;
 // Half-width of the band (in ln(e_t/e_d)) inside which an element's sign in max(0, p - q) is
 // not decided from the fp32 estimate of ln(S_t/S_d). The fp32 statistics are accurate to a
 // few 1e-6, so the exact ln(S_t/S_d) lies well inside; the pick checks that it does.
 constexpr double kBand = 3e-5;
-constexpr long long kSpinLimit = 4000000;     // polls before a wait gives up
 
-enum Mode : int { kNone = 0, kGreedy = 1, kResidual = 2, kBonus = 3 };
+// state of a sequence's outcome, as published to the final draw (0: not decided)
+enum Mode : unsigned { kNoDraw = 1, kResidual = 2, kBonus = 3 };
 
 struct RowPart {      // partial statistics of one row chunk
   float m;            // max of the raw logits in the chunk
@@ -81,37 +77,28 @@ struct PosInfo {      // what the evaluation of one (sequence, position) found
   int g;              // greedy: target argmax
 };
 
-struct SeqDesc {      // what the final draw of one sequence needs
-  int mode;           // Mode
-  int j;              // position of the final draw
-  float mt, md;       // exact maxima of target row j and draft row j
-  float lnrho;        // fp32 estimate of ln(S_t / S_d) for row j (residual only)
-  float u;            // final-draw uniform
-  float T;            // temperature
-  float pad;
+// Outcome of one sequence as published to the final-draw items: two 64-bit words, each
+// written and read in one access. A reader takes the pair only when both are set, so it needs
+// no ordering between them.
+struct SeqPub {
+  unsigned long long a;   // bits 0-1 Mode, 2-6 position j of the final draw, 32-63 bits of
+                          // the exact max of target row j
+  unsigned long long c;   // bits 0-31 bits of the exact max of draft row j, 32-63 bits of the
+                          // fp32 ln(S_t / S_d) of row j with its lowest bit forced to 1 (set
+                          // marker; moves the estimate by one ulp, far inside the band)
 };
 
-struct FinPart {      // fp64 sums of one final-draw chunk
+struct FinPart {      // fp64 sums of one final-draw item
   double st, sd;      // sum e_t, sum e_d   (e = exp((x - max) / T))
   double at, ad;      // sums over elements certainly in the positive part of p - q
   double bt, bd;      // sums over the elements inside the band
   double dmin, dmax;  // min / max of x_t - x_d inside the band (+inf / -inf: none)
 };
 
-struct Hdr {          // per-call counters of one set
-  unsigned q_seq;     // sequences queued for a final draw
-  unsigned q_items;   // final-draw items published
-  unsigned q_claim;   // final-draw items claimed by workers
-  unsigned decided;   // sequences whose outcome is decided (and queued if sampled)
-  unsigned pad[60];
-};
-
 struct CounterSet {   // everything that must be zero when a call starts
-  Hdr* hdr;
   unsigned long long* st;   // [B] done bits 0..31, reject bits 32..63
   unsigned* pc;             // [B][D+1] completed chunks of the position's rows
-  unsigned* fdone;          // [B] completed final-draw items
-  unsigned* qs;             // [B] queue slots: sequence + 1 (0 = not yet written)
+  SeqPub* pub;              // [B] outcome of the sequence (zero until decided)
 };
 
 struct Params {
@@ -127,14 +114,13 @@ struct Params {
   int R;              // rows per sequence, 2D + 1 (target 0..D, then draft 0..D-1)
   int rch;            // elements per row chunk
   int nchunk;         // row chunks per row
-  int fch;            // elements per final-draw item (multiple of 512)
+  int fch;            // elements per final-draw item (rch / kItemsPerChunk, a multiple of 512)
   int nF;             // final-draw items per sequence
-  int n_workers;      // worker workgroups (blockIdx < n_workers)
+  int n_pick;         // pick workgroups (four sequences each; they clear the next counters)
   CounterSet cur;     // this call's counters
-  CounterSet nxt;     // the next call's counters, cleared by the workers
+  CounterSet nxt;     // the next call's counters, cleared by the pick kernel
   RowPart* rpart;     // [B][R][nchunk]
   PosInfo* pinfo;     // [B][D+1]
-  SeqDesc* desc;      // [B]
   FinPart* fpart;     // [B][nF]
   double* fmass;      // [B][nF] scratch of the pick
   float* dbg_row_stats;  // optional [B][R][2]
@@ -197,7 +183,7 @@ __device__ inline uint4 load_stream(const uint4* p) {
 template <typename E> struct Run;
 template <> struct Run<uint16_t> {
   uint32_t w[4];
-  __device__ void load(const uint16_t* p, int a, int n) {
+  __device__ __forceinline__ void load(const uint16_t* p, int a, int n) {
     const uint16_t* q = p + a;
     if (n == kFinPer && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
       const uint4 v = *reinterpret_cast<const uint4*>(q);
@@ -214,10 +200,13 @@ template <> struct Run<uint16_t> {
   __device__ float at(int e) const {
     return __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
   }
+  __device__ unsigned bits(int e) const {
+    return (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu);
+  }
 };
 template <> struct Run<float> {
   float x[kFinPer];
-  __device__ void load(const float* p, int a, int n) {
+  __device__ __forceinline__ void load(const float* p, int a, int n) {
     const float* q = p + a;
     if (n == kFinPer && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
       const float4 v0 = reinterpret_cast<const float4*>(q)[0];
@@ -317,29 +306,16 @@ __device__ inline double wave_max(double x) {
 // shared memory of one workgroup
 
 struct Shared {
-  double exp_tab[256];          // 2^(i/256), workers only
-  double red[kWaves][8];
-  int flag;
+  float red[kWaves][2];         // cross-wavefront combine of the row chunk
 };
 
-// fp64 exp: e^t = 2^(k/256) * e^f with k = rint(t * 256 / ln 2) and f = t - k * ln2/256
-// (|f| <= ln2/512; ln2/256 split in two parts so that k * hi is exact), e^f from its degree-4
-// Taylor polynomial (truncation below 4e-17 relative), 2^(k/256) = tab[k mod 256] * 2^(k div 256).
-__device__ inline double exp64(double t, const double* tab) {
-  const double y = t * 369.3299304675746;                  // 256 / ln 2
-  const double kf = __builtin_rint(y);
-  double f = fma(-kf, 0.002707606172407395, t);            // ln2/256, high part
-  f = fma(-kf, 1.6548911585192516e-12, f);                 // ln2/256, low part
-  const int k = int(kf);
-  const double p = fma(fma(fma(fma(f, 1.0 / 24.0, 1.0 / 6.0), f, 0.5), f, 1.0), f, 1.0);
-  return ldexp(tab[k & 255] * p, k >> 8);
-}
+
 
 // ------------------------------------------------------------------------------------------
-// outcome of a sequence (wavefront 0 of the deciding workgroup)
+// outcome of a sequence (one wavefront of the deciding workgroup)
 
 template <typename E>
-__device__ void decide(const Params& P, int b, int L, float T, bool greedy, int j, int lane) {
+__device__ __forceinline__ void decide(const Params& P, int b, int L, float T, bool greedy, int j, int lane) {
   const int D = P.D;
   const int32_t* xs = P.tokens + size_t(b) * D;
   int32_t* toks = P.out_tokens + size_t(b) * (D + 1);
@@ -348,7 +324,7 @@ __device__ void decide(const Params& P, int b, int L, float T, bool greedy, int 
     for (int i = lane; i <= D; i += 64) toks[i] = -1;
     if (lane == 0) {
       P.out_len[b] = 0;
-      add_dev(&P.cur.hdr->decided, 1u);
+      st_dev(&P.cur.pub[b].a, (unsigned long long)kNoDraw);
     }
     return;
   }
@@ -357,7 +333,7 @@ __device__ void decide(const Params& P, int b, int L, float T, bool greedy, int 
       toks[i] = (i <= j) ? ld_dev(&P.pinfo[size_t(b) * (D + 1) + i].g) : -1;
     if (lane == 0) {
       P.out_len[b] = j + 1;
-      add_dev(&P.cur.hdr->decided, 1u);
+      st_dev(&P.cur.pub[b].a, (unsigned long long)kNoDraw);
     }
     return;
   }
@@ -365,32 +341,23 @@ __device__ void decide(const Params& P, int b, int L, float T, bool greedy, int 
     if (i < j) toks[i] = xs[i];
     else if (i > j) toks[i] = -1;      // position j is written by the final draw
   }
+  // publish the final draw's descriptor (two self-validating words)
   if (lane == 0) {
     P.out_len[b] = j + 1;
     const PosInfo* pi = P.pinfo + size_t(b) * (D + 1) + j;
-    SeqDesc* d = P.desc + b;
-    st_dev(&d->mode, int(j < L ? kResidual : kBonus));
-    st_dev(&d->j, j);
-    st_dev(&d->mt, ld_dev(&pi->mt));
-    st_dev(&d->md, j < L ? ld_dev(&pi->md) : 0.f);
-    st_dev(&d->lnrho, j < L ? ld_dev(&pi->lnrho) : 0.f);
-    st_dev(&d->u, P.uniforms[size_t(b) * (D + 1) + D]);
-    st_dev(&d->T, T);
-    wait_stores();
-    const unsigned slot = add_dev(&P.cur.hdr->q_seq, 1u);
-    st_dev(P.cur.qs + slot, unsigned(b + 1));
-    wait_stores();
-    add_dev(&P.cur.hdr->q_items, unsigned(P.nF));
-    add_dev(&P.cur.hdr->decided, 1u);
+    const bool res = j < L;
+    const unsigned mt = __float_as_uint(ld_dev(&pi->mt));
+    const unsigned md = res ? __float_as_uint(ld_dev(&pi->md)) : 0u;
+    const unsigned lr = (res ? __float_as_uint(ld_dev(&pi->lnrho)) : 0u) | 1u;
+    st_dev(&P.cur.pub[b].c, ((unsigned long long)lr << 32) | md);
+    st_dev(&P.cur.pub[b].a, ((unsigned long long)mt << 32) |
+                                (unsigned long long)((res ? kResidual : kBonus) | (j << 2)));
   }
 }
 
-// Evaluation of position p of sequence b once all its chunks are in (whole workgroup calls it;
-// wavefront 0 does the work).
+// Evaluation of position p of sequence b once all its chunks are in (one wavefront).
 template <typename E>
-__device__ void evaluate(const Params& P, int b, int p, int L, float T, bool greedy, int tid) {
-  if (tid >= 64) return;
-  const int lane = tid;
+__device__ __forceinline__ void evaluate(const Params& P, int b, int p, int L, float T, bool greedy, int lane) {
   const int D = P.D, R = P.R, nc = P.nchunk;
   const RowPart* tpart = P.rpart + (size_t(b) * R + p) * nc;
   const RowPart* dpart = P.rpart + (size_t(b) * R + D + 1 + p) * nc;
@@ -466,37 +433,14 @@ __device__ void evaluate(const Params& P, int b, int p, int L, float T, bool gre
 }
 
 // ------------------------------------------------------------------------------------------
-// row workgroup
+// row chunk: statistics of one 32 KB chunk (whole workgroup), then the pair counter and the
+// evaluation (wavefront 0 only; the other wavefronts return after the combine)
 
 template <typename E>
-__device__ void row_workgroup(const Params& P, Shared& sm, long long rid, int tid) {
+__device__ __forceinline__ void row_chunk(const Params& P, Shared& sm, int b, int p, int which, int c, int L,
+                          float T, bool greedy, int tid) {
   constexpr int kV = Elem<E>::kVec;
-  const int nc = P.nchunk;
-  const long long per_p = (long long)P.B * 2 * nc;
-  const int p = int(rid / per_p);
-  const long long rem = rid - (long long)p * per_p;
-  const int b = int(rem / (2 * nc));
-  const int which = int(rem % (2 * nc)) / nc;          // 0 target row p, 1 draft row p
-  const int c = int(rem % nc);
-  const int D = P.D;
-  const int L = P.lens ? P.lens[b] : D;
-  const float T = P.temperature[b];
-
-  if (!seq_valid(L, D, T)) {
-    // invalid length or temperature: one workgroup of the sequence marks the row
-    if (p == 0 && which == 0 && c == 0) {
-      int32_t* toks = P.out_tokens + size_t(b) * (D + 1);
-      for (int i = tid; i <= D; i += kThreads) toks[i] = -1;
-      if (tid == 0) {
-        P.out_len[b] = 0;
-        add_dev(&P.cur.hdr->decided, 1u);
-      }
-    }
-    return;
-  }
-  const bool greedy = (T == 0.f);
-  if (which == 0 ? (p > L) : (greedy || p >= L)) return;   // row not needed
-
+  const int D = P.D, nc = P.nchunk;
   const int r = which == 0 ? p : D + 1 + p;
   const E* row = which == 0
       ? static_cast<const E*>(P.target) + (size_t(b) * (D + 1) + p) * size_t(P.V)
@@ -519,6 +463,7 @@ __device__ void row_workgroup(const Params& P, Shared& sm, long long rid, int ti
     if (x >= c0 && x < c0 + n) xv = Elem<E>::get(row, x);
   }
 
+  const int wave = tid >> 6;
   float m, s;
   if (greedy) {
     float best = -INFINITY;
@@ -536,12 +481,10 @@ __device__ void row_workgroup(const Params& P, Shared& sm, long long rid, int ti
     }
     for (int i = nvec * kV + tid; i < n; i += kThreads) am_combine(best, bi, Elem<E>::get(ptr, i), i);
     wave_am(best, bi);
-    float* rv = reinterpret_cast<float*>(&sm.red[0][0]);
-    int* ri = reinterpret_cast<int*>(&sm.red[0][4]);
-    if ((tid & 63) == 0) { rv[tid >> 6] = best; ri[tid >> 6] = bi; }
+    if ((tid & 63) == 0) { sm.red[wave][0] = best; sm.red[wave][1] = __int_as_float(bi); }
     __syncthreads();
-    if (tid == 0)
-      for (int w = 1; w < kWaves; ++w) am_combine(best, bi, rv[w], ri[w]);
+    if (wave != 0) return;
+    for (int w = 1; w < kWaves; ++w) am_combine(best, bi, sm.red[w][0], __float_as_int(sm.red[w][1]));
     m = best;
     s = __int_as_float(bi < 0 ? -1 : c0 + bi);
   } else {
@@ -576,41 +519,94 @@ __device__ void row_workgroup(const Params& P, Shared& sm, long long rid, int ti
       sum += __builtin_amdgcn_exp2f((x - mx) * k2);
     }
     wave_ms(mx, sum, k2);
-    float* rm = reinterpret_cast<float*>(&sm.red[0][0]);
-    float* rs = reinterpret_cast<float*>(&sm.red[0][4]);
-    if ((tid & 63) == 0) { rm[tid >> 6] = mx; rs[tid >> 6] = sum; }
+    if ((tid & 63) == 0) { sm.red[wave][0] = mx; sm.red[wave][1] = sum; }
     __syncthreads();
-    if (tid == 0)
-      for (int w = 1; w < kWaves; ++w) ms_combine(mx, sum, rm[w], rs[w], k2);
+    if (wave != 0) return;
+    for (int w = 1; w < kWaves; ++w) ms_combine(mx, sum, sm.red[w][0], sm.red[w][1], k2);
     m = mx;
     s = sum;
   }
 
-  if (tid == 0) {
+  // wavefront 0: publish the partial, count the pair's chunks, evaluate after the last one
+  const int lane = tid;
+  int last = 0;
+  if (lane == 0) {
     RowPart* out = P.rpart + (size_t(b) * P.R + r) * nc + c;
     st_dev(&out->m, m);
     st_dev(&out->s, s);
     st_dev(&out->xv, xv);
     wait_stores();
     const unsigned done = add_dev(P.cur.pc + size_t(b) * (D + 1) + p, 1u) + 1u;
-    sm.flag = (done == unsigned(pair_chunks(p, L, greedy, nc))) ? 1 : 0;
+    last = (done == unsigned(pair_chunks(p, L, greedy, nc))) ? 1 : 0;
   }
-  __syncthreads();
-  if (sm.flag) evaluate<E>(P, b, p, L, T, greedy, tid);
+  if (uniform(__shfl(last, 0))) evaluate<E>(P, b, p, L, T, greedy, lane);
 }
 
 // ------------------------------------------------------------------------------------------
-// final draw (wave-level workers)
+// final draw
 //
-// A final-draw item covers fch consecutive elements (fch a multiple of 512) of the final row(s)
-// of one sequence. Inside an item, block k holds elements [512k, 512k + 512) and lane l of the
-// wavefront handles elements 512k + 8l .. 512k + 8l + 7 of each block (16-byte loads).
+// A final-draw item covers kItemElems<E> consecutive elements of the final row(s) of one
+// sequence (2048 bf16 or 1024 fp32 logits), in blocks of 512: lane l handles elements
+// 512k + 8l .. 512k + 8l + 7 of block k, and loads all of them at once. One wavefront per item.
+//
+// Weights are e(x) = exp((x - m) / T) in fp64 (m the row's exact max). Exponents are carried in
+// units of ln2/256: y = (x - m) / T * 256 / ln 2 = fma(x, c1, c0) with c1 = 256 / (T ln 2) and
+// c0 = -m c1, so that e = 2^(y / 256); for |x - m| / T up to 30 the rounding of c1, c0 and of
+// the fma moves y by a few 1e-12, i.e. e by a few 1e-15 relative.
+
+template <typename E>
+constexpr int kItemElems = kRowChunkBytes / int(sizeof(E)) / kItemsPerChunk;
+template <typename E>
+constexpr int kItemBlocks = kItemElems<E> / kFinBlock;
+
+// 2^(y / 256) = 2^(k / 256) * 2^(r / 256), k = rint(y), r = y - k in [-1/2, 1/2] (exact);
+// 2^(r / 256) = e^(r ln2 / 256) from its degree-4 Taylor polynomial in r (truncation below
+// 4e-17 relative); 2^(k / 256) = e2[k mod 256] * 2^(k div 256). Arguments far below zero give
+// 0 (the integer conversion saturates and ldexp underflows).
+__device__ inline double exp2k(double y, const double* e2) {
+  constexpr double c = 0.0027076061740622863;          // ln2 / 256
+  constexpr double p1 = c, p2 = c * c / 2, p3 = c * c * c / 6, p4 = c * c * c * c / 24;
+  const double kf = __builtin_rint(y);
+  const double r = y - kf;
+  const int k = int(kf);
+  const double p = fma(fma(fma(fma(r, p4, p3), r, p2), r, p1), r, 1.0);
+  return ldexp(e2[k & 255] * p, k >> 8);
+}
+
+// e(x) of one final row.
+struct RowExp {
+  double c1, c0;        // y = fma(x, c1, c0)
+  const double* e2;     // 2^(i/256), shared memory
+  __device__ double operator()(float x) const { return exp2k(fma(double(x), c1, c0), e2); }
+};
 
 struct Draw {           // what the fp64 evaluation of one sequence's final row(s) needs
   bool residual;
   int j;
-  double mt, md, invT, lnrho, u;
+  RowExp t, d;          // target row j, draft row j
+  double dhi, dlo;      // band of x_t - x_d: T (ln(rho~) +/- kBand) + m_t - m_d
+  double lnrho, u;
 };
+
+// The draw of sequence b from its published words (wave-uniform arguments); e2 in shared memory.
+__device__ inline Draw make_draw(const Params& P, int b, unsigned long long a,
+                                 unsigned long long c, const double* e2) {
+  constexpr double k256 = 369.3299304675746;          // 256 / ln 2
+  Draw w;
+  w.residual = unsigned(a & 3u) == kResidual;
+  w.j = int((a >> 2) & 31u);
+  const double T = double(P.temperature[b]);
+  w.u = double(P.uniforms[size_t(b) * (P.D + 1) + P.D]);
+  w.lnrho = double(__uint_as_float(unsigned(c >> 32)));
+  const double mt = double(__uint_as_float(unsigned(a >> 32)));
+  const double md = double(__uint_as_float(unsigned(c)));
+  const double c1 = k256 / T;
+  w.t = RowExp{c1, -mt * c1, e2};
+  w.d = RowExp{c1, -md * c1, e2};
+  w.dhi = T * (w.lnrho + kBand) + (mt - md);
+  w.dlo = T * (w.lnrho - kBand) + (mt - md);
+  return w;
+}
 
 template <typename E>
 __device__ inline const E* final_row(const Params& P, int b, int j, bool draft) {
@@ -618,13 +614,27 @@ __device__ inline const E* final_row(const Params& P, int b, int j, bool draft) 
                : static_cast<const E*>(P.target) + (size_t(b) * (P.D + 1) + j) * size_t(P.V);
 }
 
+// One lane's elements of one item: block k holds elements a0 + 512k + 8 lane + (0..7).
+template <typename E>
+struct ItemRuns {
+  Run<E> r[kItemBlocks<E>];
+  __device__ __forceinline__ void load(const E* row, int a0, int V, int lane) {
+#pragma unroll
+    for (int k = 0; k < kItemBlocks<E>; ++k) {
+      const int a = a0 + kFinBlock * k + kFinPer * lane;
+      const int n = max(0, min(kFinPer, V - a));
+      if (n > 0) r[k].load(row, a, n);
+    }
+  }
+};
+
 // Exact weight of element e of the runs: e_t when target_only, else max(0, e_t/S_t - e_d/S_d).
 template <typename E>
 __device__ inline double exact_weight(const Run<E>& rt, const Run<E>& rd, int e, const Draw& w,
-                                      bool target_only, double it, double id, const double* tab) {
-  const double et = exp64((double(rt.at(e)) - w.mt) * w.invT, tab);
+                                      bool target_only, double it, double id) {
+  const double et = w.t(rt.at(e));
   if (target_only) return et;
-  const double ed = exp64((double(rd.at(e)) - w.md) * w.invT, tab);
+  const double ed = w.d(rd.at(e));
   return fmax(0.0, et * it - ed * id);
 }
 
@@ -638,211 +648,209 @@ __device__ inline double wave_inclusive_scan(double x, int lane) {
   return x;
 }
 
-// Sum of the exact weights of one item's elements (fixed order); target_only as above.
+// Sum of the exact weights of one item's elements (fixed order); target_only as above. Only
+// for the rare sequences whose band did not resolve every element.
 template <typename E>
 __device__ inline double item_exact_mass(const Params& P, const E* trow, const E* drow,
                                          const Draw& w, int f, bool target_only, double it,
-                                         double id, const double* tab, int lane) {
-  const int a0 = f * P.fch;
-  const int nblk = (min(P.fch, P.V - a0) + 511) / 512;
+                                         double id, int lane) {
+  const int a0 = f * kItemElems<E>;
+  ItemRuns<E> t, d;
+  t.load(trow, a0, P.V, lane);
+  if (!target_only) d.load(drow, a0, P.V, lane);
   double s = 0.0;
-  for (int k = 0; k < nblk; ++k) {
-    const int a = a0 + 512 * k + 8 * lane;
-    const int n = max(0, min(kFinPer, P.V - a));
-    if (n > 0) {
-      Run<E> rt, rd;
-      rt.load(trow, a, n);
-      if (!target_only) rd.load(drow, a, n);
 #pragma unroll
-      for (int e = 0; e < kFinPer; ++e) {
-        if (e < n) s += exact_weight<E>(rt, rd, e, w, target_only, it, id, tab);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+  for (int k = 0; k < kItemBlocks<E>; ++k) {
+    const int n = max(0, min(kFinPer, P.V - (a0 + kFinBlock * k + kFinPer * lane)));
+#pragma unroll
+    for (int e = 0; e < kFinPer; ++e) {
+      if (e < n) s += exact_weight<E>(t.r[k], d.r[k], e, w, target_only, it, id);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   return wave_sum(s);
 }
 
 // The last final-draw item of a sequence: exact normalisers, item masses, token (one wavefront).
+// Up to 64 items the item records are read once, one per lane; beyond, they are re-read per pass.
 template <typename E>
-__device__ void wave_pick(const Params& P, const double* tab, int b, const Draw& w, int lane) {
+__device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w, int lane) {
   const int nF = P.nF;
   const FinPart* fp = P.fpart + size_t(b) * nF;
-  double* mass = P.fmass + size_t(b) * nF;
+  double* xmass = P.fmass + size_t(b) * nF;          // exact item masses of the slow path
   const E* trow = final_row<E>(P, b, w.j, false);
   const E* drow = w.residual ? final_row<E>(P, b, w.j, true) : trow;
+  const bool one = nF <= 64;
+  FinPart r = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, INFINITY, -INFINITY};
+  if (one && lane < nF) {
+    const double* q = reinterpret_cast<const double*>(fp + lane);
+    r.st = ld_dev(q + 0); r.sd = ld_dev(q + 1); r.at = ld_dev(q + 2); r.ad = ld_dev(q + 3);
+    r.bt = ld_dev(q + 4); r.bd = ld_dev(q + 5); r.dmin = ld_dev(q + 6); r.dmax = ld_dev(q + 7);
+  }
+  // the record of item f (f = lane + 64 k, this lane's)
+  auto rec = [&](int f) {
+    if (one) return r;
+    FinPart x = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, INFINITY, -INFINITY};
+    if (f < nF) {
+      const double* q = reinterpret_cast<const double*>(fp + f);
+      x.st = ld_dev(q + 0); x.sd = ld_dev(q + 1); x.at = ld_dev(q + 2); x.ad = ld_dev(q + 3);
+      x.bt = ld_dev(q + 4); x.bd = ld_dev(q + 5); x.dmin = ld_dev(q + 6); x.dmax = ld_dev(q + 7);
+    }
+    return x;
+  };
 
   double st = 0.0, sd = 0.0;
   int multi = 0;
-  for (int f = lane; f < nF; f += 64) {
-    st += ld_dev(&fp[f].st);
-    sd += ld_dev(&fp[f].sd);
-    if (ld_dev(&fp[f].dmin) < ld_dev(&fp[f].dmax)) multi = 1;
+  for (int base = 0; base < nF; base += 64) {
+    const FinPart x = rec(base + lane);
+    st += x.st;
+    sd += x.sd;
+    if (x.dmin < x.dmax) multi = 1;
   }
   st = wave_sum(st);
   sd = wave_sum(sd);
   const double it = 1.0 / st, id = 1.0 / sd;
-  // did the band hold the exact ratio, and is every item's in-band set one ratio class?
-  const bool slow = w.residual && (__any(multi) || !(fabs(log(st / sd) - w.lnrho) < kBand));
-
-  bool target_only = !w.residual;
-  if (!slow) {
-    for (int f = lane; f < nF; f += 64) {
-      double m;
-      if (target_only) {
-        m = ld_dev(&fp[f].st);
-      } else {
-        m = ld_dev(&fp[f].at) * it - ld_dev(&fp[f].ad) * id;
-        if (ld_dev(&fp[f].dmin) <= ld_dev(&fp[f].dmax))            // one in-band ratio class
-          m += fmax(0.0, ld_dev(&fp[f].bt) * it - ld_dev(&fp[f].bd) * id);
-        m = fmax(0.0, m);
-      }
-      st_dev(mass + f, m);
-    }
-  } else {
+  // did the band hold the exact ratio (with room for the rounding of its bounds), and is every
+  // item's in-band set one ratio class?
+  const bool slow = w.residual && (__any(multi) || !(fabs(log(st / sd) - w.lnrho) < 0.5 * kBand));
+  if (slow) {
     for (int f = 0; f < nF; ++f) {
-      const double m = item_exact_mass<E>(P, trow, drow, w, f, false, it, id, tab, lane);
-      if (lane == 0) st_dev(mass + f, m);
-    }
-  }
-  wait_stores();
-
-  // inclusive prefix of the item masses (64 at a time); Z is the last prefix
-  auto prefix = [&](bool from_st) {
-    double total = 0.0;
-    for (int base = 0; base < nF; base += 64) {
-      const int f = base + lane;
-      const double v = (f < nF) ? (from_st ? ld_dev(&fp[f].st) : ld_dev(mass + f)) : 0.0;
-      const double inc = wave_inclusive_scan(v, lane) + total;
-      if (f < nF) st_dev(mass + f, inc);
-      total = __shfl(inc, 63);
+      const double m = item_exact_mass<E>(P, trow, drow, w, f, false, it, id, lane);
+      if (lane == 0) st_dev(xmass + f, m);
     }
     wait_stores();
-    return total;
+  }
+  bool target_only = !w.residual;
+  // mass of item f: normalised residual, or unnormalised p (bonus draw, zero-mass fallback)
+  auto mass = [&](int f) {
+    if (f >= nF) return 0.0;
+    if (slow && !target_only) return ld_dev(xmass + f);
+    const FinPart x = rec(f);
+    if (target_only) return x.st;
+    double m = x.at * it - x.ad * id;
+    if (x.dmin <= x.dmax) m += fmax(0.0, x.bt * it - x.bd * id);   // one in-band ratio class
+    return fmax(0.0, m);
   };
-  double total = prefix(false);
-  if (!(total > 0.0) && !target_only) {
-    target_only = true;                // residual of zero mass (rounding only): draw from p_j
-    total = prefix(true);
-  }
-  const double t = w.u * total;
 
-  // first item whose inclusive prefix exceeds t (else the last item with positive mass)
-  int fstar = nF, flast = -1;
-  for (int base = 0; base < nF; base += 64) {
+  // Z, then the first item whose inclusive prefix exceeds t = u Z (else the last item with
+  // positive mass), 64 items at a time
+  double Z = 0.0;
+  for (int base = 0; base < nF; base += 64) Z += wave_sum(mass(base + lane));
+  if (!(Z > 0.0) && !target_only) {
+    target_only = true;                // residual of zero mass (rounding only): draw from p_j
+    Z = 0.0;
+    for (int base = 0; base < nF; base += 64) Z += wave_sum(mass(base + lane));
+  }
+  const double t = w.u * Z;
+  int fstar = -1, flast = -1;
+  double run = 0.0, total = 0.0;
+  for (int base = 0; base < nF && fstar < 0; base += 64) {
     const int f = base + lane;
-    const double inc = (f < nF) ? ld_dev(mass + f) : 0.0;
-    const double prev = (f > 0 && f < nF) ? ld_dev(mass + f - 1) : 0.0;
+    const double m = mass(f);
+    const double inc = wave_inclusive_scan(m, lane) + total;
     const unsigned long long over = __ballot(f < nF && inc > t);
-    const unsigned long long pos = __ballot(f < nF && inc > prev);
-    if (over && fstar == nF) fstar = base + __builtin_ctzll(over);
+    const unsigned long long pos = __ballot(f < nF && m > 0.0);
     if (pos) flast = base + 63 - __builtin_clzll(pos);
+    if (over) {
+      const int l = __builtin_ctzll(over);
+      fstar = base + l;
+      run = __shfl(inc - m, l);
+    }
+    total = __shfl(inc, 63);
   }
-  const bool past_end = (fstar >= nF);
-  if (past_end) fstar = flast;
+  const bool past_end = fstar < 0;
   int32_t* out = P.out_tokens + size_t(b) * (P.D + 1) + w.j;
-  if (fstar < 0) {                     // no positive weight at all
-    if (lane == 0) *out = -1;
-    return;
+  if (past_end) {
+    fstar = flast;
+    if (fstar < 0) {                   // no positive weight at all
+      if (lane == 0) *out = -1;
+      return;
+    }
   }
-  double run = (fstar > 0) ? ld_dev(mass + fstar - 1) : 0.0;
 
   // rescan the chosen item block by block, in ascending element order
-  const int a0 = fstar * P.fch;
-  const int nblk = (min(P.fch, P.V - a0) + 511) / 512;
+  const int a0 = fstar * kItemElems<E>;
+  ItemRuns<E> tr, dr;
+  tr.load(trow, a0, P.V, lane);
+  if (!target_only) dr.load(drow, a0, P.V, lane);
   int found = -1, last_pos = -1;
-  for (int k = 0; k < nblk && found < 0; ++k) {
-    const int a = a0 + 512 * k + 8 * lane;
-    const int n = max(0, min(kFinPer, P.V - a));
-    Run<E> rt, rd;
-    double ls = 0.0;
-    int my_last = -1;
-    if (n > 0) {
-      rt.load(trow, a, n);
-      if (!target_only) rd.load(drow, a, n);
+#pragma unroll
+  for (int k = 0; k < kItemBlocks<E>; ++k) {
+    if (found < 0) {                   // wave-uniform
+      const int a = a0 + kFinBlock * k + kFinPer * lane;
+      const int n = max(0, min(kFinPer, P.V - a));
+      double ls = 0.0;
+      int my_last = -1;
 #pragma unroll
       for (int e = 0; e < kFinPer; ++e) {
         if (e < n) {
-          const double wt = exact_weight<E>(rt, rd, e, w, target_only, it, id, tab);
+          const double wt = exact_weight<E>(tr.r[k], dr.r[k], e, w, target_only, it, id);
           ls += wt;
           if (wt > 0.0) my_last = a + e;
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    const double inc = wave_inclusive_scan(ls, lane) + run;
-    const double pre = inc - ls;
-    // lane l owns [prefix before l, prefix through l): consecutive stored values, one owner
-    const double lo = __shfl_up(inc, 1);
-    const double mylo = (lane == 0) ? run : lo;
-    last_pos = max(last_pos, my_last);
-    const bool owner = !past_end && ls > 0.0 && mylo <= t && t < inc;
-    (void)pre;
-    const unsigned long long own = __ballot(owner);
-    if (own) {
-      const int ol = __builtin_ctzll(own);
-      int k2 = -1;
-      if (lane == ol) {
-        double acc = mylo;
+      const double inc = wave_inclusive_scan(ls, lane) + run;
+      // lane l owns [prefix before l, prefix through l): consecutive stored values, one owner
+      const double lo = __shfl_up(inc, 1);
+      const double mylo = (lane == 0) ? run : lo;
+      last_pos = max(last_pos, my_last);
+      const bool owner = !past_end && ls > 0.0 && mylo <= t && t < inc;
+      const unsigned long long own = __ballot(owner);
+      if (own) {
+        const int ol = __builtin_ctzll(own);
+        int k2 = -1;
+        if (lane == ol) {
+          double acc = mylo;
 #pragma unroll
-        for (int e = 0; e < kFinPer; ++e) {
-          if (e < n && k2 < 0) {
-            acc += exact_weight<E>(rt, rd, e, w, target_only, it, id, tab);
-            if (acc > t) k2 = a + e;
+          for (int e = 0; e < kFinPer; ++e) {
+            if (e < n && k2 < 0) {
+              acc += exact_weight<E>(tr.r[k], dr.r[k], e, w, target_only, it, id);
+              if (acc > t) k2 = a + e;
+            }
           }
-          __builtin_amdgcn_sched_barrier(0);
+          if (k2 < 0) k2 = my_last;
         }
-        if (k2 < 0) k2 = my_last;
+        found = __shfl(k2, ol);
       }
-      found = __shfl(k2, ol);
+      run = __shfl(inc, 63);
     }
-    run = __shfl(inc, 63);
   }
   // rounding put u * Z past the end: the last element with positive weight
   for (int off = 32; off > 0; off >>= 1) last_pos = max(last_pos, __shfl_xor(last_pos, off));
   if (lane == 0) *out = (found >= 0) ? found : last_pos;
 }
 
+// fp64 partial sums of item f of sequence b from the lane's runs, stored to the item's record
+// (no wait).
 template <typename E>
-__device__ void wave_fin_item(const Params& P, const double* tab, int b, int f, const Draw& w,
-                              int lane) {
-  const E* trow = final_row<E>(P, b, w.j, false);
-  const E* drow = w.residual ? final_row<E>(P, b, w.j, true) : trow;
-  const int a0 = f * P.fch;
-  const int nblk = (min(P.fch, P.V - a0) + 511) / 512;
-  const double hi = w.lnrho + kBand, lo = w.lnrho - kBand;
+__device__ __forceinline__ void item_sums(const Params& P, int b, int f, const Draw& w,
+                                          const ItemRuns<E>& tr, const ItemRuns<E>& dr,
+                                          int lane) {
+  const int a0 = f * kItemElems<E>;
   double st = 0, sd = 0, at = 0, ad = 0, bt = 0, bd = 0, dmin = INFINITY, dmax = -INFINITY;
-  for (int k = 0; k < nblk; ++k) {
-    const int a = a0 + 512 * k + 8 * lane;
-    const int n = max(0, min(kFinPer, P.V - a));
-    if (n <= 0) continue;
-    Run<E> rt, rd;
-    rt.load(trow, a, n);
-    if (w.residual) rd.load(drow, a, n);
+#pragma unroll
+  for (int k = 0; k < kItemBlocks<E>; ++k) {
+    const int n = max(0, min(kFinPer, P.V - (a0 + kFinBlock * k + kFinPer * lane)));
 #pragma unroll
     for (int e = 0; e < kFinPer; ++e) {
       if (e >= n) continue;
-      const double xt = double(rt.at(e));
-      const double tt = (xt - w.mt) * w.invT;
-      const double et = exp64(tt, tab);
+      const double et = w.t(tr.r[k].at(e));
       st += et;
       if (w.residual) {
-        const double xd = double(rd.at(e));
-        const double td = (xd - w.md) * w.invT;
-        const double ed = exp64(td, tab);
+        const double ed = w.d(dr.r[k].at(e));
         sd += ed;
-        const double l = tt - td;                      // ln(e_t / e_d)
-        if (l > hi) {
-          at += et;
-          ad += ed;
-        } else if (l >= lo) {
+        // x_t - x_d against the band: above it the element is certainly in the positive part
+        const double dx = double(tr.r[k].at(e)) - double(dr.r[k].at(e));
+        const double above = dx > w.dhi ? 1.0 : 0.0;
+        at = fma(above, et, at);
+        ad = fma(above, ed, ad);
+        if (dx <= w.dhi && dx >= w.dlo) {              // inside the band (rare)
           bt += et;
           bd += ed;
-          dmin = fmin(dmin, xt - xd);
-          dmax = fmax(dmax, xt - xd);
+          dmin = fmin(dmin, dx);
+          dmax = fmax(dmax, dx);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);   // one element at a time: bounded register use
     }
   }
   st = wave_sum(st);
@@ -853,119 +861,130 @@ __device__ void wave_fin_item(const Params& P, const double* tab, int b, int f, 
   bd = wave_sum(bd);
   dmin = wave_min(dmin);
   dmax = wave_max(dmax);
-  int last = 0;
-  if (lane == 0) {
-    FinPart* out = P.fpart + size_t(b) * P.nF + f;
-    st_dev(&out->st, st);
-    st_dev(&out->sd, sd);
-    st_dev(&out->at, at);
-    st_dev(&out->ad, ad);
-    st_dev(&out->bt, bt);
-    st_dev(&out->bd, bd);
-    st_dev(&out->dmin, dmin);
-    st_dev(&out->dmax, dmax);
-    wait_stores();
-    last = (add_dev(P.cur.fdone + b, 1u) + 1u == unsigned(P.nF)) ? 1 : 0;
-  }
-  last = __shfl(last, 0);
-  if (last) wave_pick<E>(P, tab, b, w, lane);
-}
-
-// One worker wavefront. Wavefront gw owns the queue items gw, gw + W, gw + 2W, ... (W = all
-// worker wavefronts) and takes them in that order, waiting for each to be published when the
-// final-draw kernel runs alongside the row kernel. It stops at the first owned item that can
-// no longer appear (every sequence decided and the item beyond the last published one).
-template <typename E>
-__device__ void wave_worker(const Params& P, const double* tab, int gw, int lane) {
-  const unsigned nF = unsigned(P.nF);
-  const unsigned W = unsigned(P.n_workers) * kWaves;
-  int cur_b = -1;
-  Draw w = {};
-  for (unsigned u = unsigned(gw);; u += W) {
-    int b = -1;
-    if (lane == 0) {
-      long long spins = 0;
-      bool go = false;
-      for (;;) {
-        if (u < ld_dev(&P.cur.hdr->q_items)) { go = true; break; }
-        if (ld_dev(&P.cur.hdr->decided) >= unsigned(P.B) && u >= ld_dev(&P.cur.hdr->q_items)) break;
-        if (++spins > kSpinLimit) break;               // never expected: give up, do not hang
-        __builtin_amdgcn_s_sleep(8);
-      }
-      if (go) {
-        const unsigned slot = u / nF;
-        unsigned q = 0;
-        for (spins = 0; (q = ld_dev(P.cur.qs + slot)) == 0u && spins < kSpinLimit; ++spins)
-          __builtin_amdgcn_s_sleep(1);
-        b = int(q) - 1;
-      }
-    }
-    b = uniform(__shfl(b, 0));
-    if (b < 0) break;
-    const int f = int(u % nF);
-    if (b != cur_b) {                  // descriptor fields, one per lane, in one round trip
-      const SeqDesc* d = P.desc + b;
-      int iv = 0;
-      float fv = 0.f;
-      if (lane == 0) iv = ld_dev(&d->mode);
-      if (lane == 1) iv = ld_dev(&d->j);
-      if (lane == 2) fv = ld_dev(&d->mt);
-      if (lane == 3) fv = ld_dev(&d->md);
-      if (lane == 4) fv = ld_dev(&d->lnrho);
-      if (lane == 5) fv = ld_dev(&d->u);
-      if (lane == 6) fv = ld_dev(&d->T);
-      w.residual = uniform(__shfl(iv, 0)) == kResidual;
-      w.j = uniform(__shfl(iv, 1));
-      w.mt = uniform(double(__shfl(fv, 2)));
-      w.md = uniform(double(__shfl(fv, 3)));
-      w.lnrho = uniform(double(__shfl(fv, 4)));
-      w.u = uniform(double(__shfl(fv, 5)));
-      w.invT = uniform(1.0 / double(__shfl(fv, 6)));
-      cur_b = b;
-    }
-    wave_fin_item<E>(P, tab, b, f, w, lane);
+  // every lane holds the same totals (butterfly reductions); lane k stores field k
+  if (lane < 8) {
+    const double v = lane == 0 ? st : lane == 1 ? sd : lane == 2 ? at : lane == 3 ? ad
+                   : lane == 4 ? bt : lane == 5 ? bd : lane == 6 ? dmin : dmax;
+    st_dev(reinterpret_cast<double*>(P.fpart + size_t(b) * P.nF + f) + lane, v);
   }
 }
 
-template <typename E>
-__device__ void worker(const Params& P, Shared& sm, int wid, int tid) {
-  for (int i = tid; i < 256; i += kThreads) sm.exp_tab[i] = exp2(double(i) / 256.0);
+__device__ inline unsigned long long uniform64(unsigned long long v) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane(unsigned(v));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(unsigned(v >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
 
-  // clear the counters of the next call (no workgroup of this call touches them)
-  {
-    const long long stride = (long long)P.n_workers * kThreads;
-    const long long me = (long long)wid * kThreads + tid;
-    for (long long i = me; i < P.B; i += stride) {
-      st_dev(P.nxt.st + i, 0ull);
-      st_dev(P.nxt.fdone + i, 0u);
-      st_dev(P.nxt.qs + i, 0u);
-    }
-    const long long npc = (long long)P.B * (P.D + 1);
-    for (long long i = me; i < npc; i += stride) st_dev(P.nxt.pc + i, 0u);
-    if (wid == 0 && tid < 4) st_dev(reinterpret_cast<unsigned*>(P.nxt.hdr) + tid, 0u);
-  }
-  __syncthreads();
-  wave_worker<E>(P, sm.exp_tab, wid * kWaves + (tid >> 6), tid & 63);
+// Does a sequence's published pair (a, c) call for a final draw that items can start on?
+__device__ inline bool draw_ready(unsigned long long a, unsigned long long c) {
+  return unsigned(a & 3u) >= kResidual && ((c >> 32) & 1u);
 }
 
 // ------------------------------------------------------------------------------------------
-// the kernel
+// workgroups
 
-// Row kernel: one workgroup per row chunk (its own register budget, so many stay resident).
+template <typename E>
+__device__ __forceinline__ void row_workgroup(const Params& P, Shared& sm, int rid, int tid) {
+  const int nc = P.nchunk;
+  const int per_p = P.B * 2 * nc;
+  const int p = rid / per_p;
+  const int local = rid - p * per_p;
+  const int b = local / (2 * nc);
+  const int which = (local % (2 * nc)) / nc;          // 0 target row p, 1 draft row p
+  const int c = local % nc;
+  const int D = P.D;
+  const int L = P.lens ? P.lens[b] : D;
+  const float T = P.temperature[b];
+  if (!seq_valid(L, D, T)) {
+    // invalid length or temperature: one wavefront of the sequence marks the row
+    if (p == 0 && which == 0 && c == 0 && tid < 64) {
+      int32_t* toks = P.out_tokens + size_t(b) * (D + 1);
+      for (int i = tid; i <= D; i += 64) toks[i] = -1;
+      if (tid == 0) {
+        P.out_len[b] = 0;
+        st_dev(&P.cur.pub[b].a, (unsigned long long)kNoDraw);
+      }
+    }
+    return;
+  }
+  const bool greedy = (T == 0.f);
+  if (which == 0 ? (p <= L) : (!greedy && p < L))      // rows the method needs
+    row_chunk<E>(P, sm, b, p, which, c, L, T, greedy, tid);
+}
+
+// Final-draw item wavefront: item g = b * nF + f, after the row kernel (every sequence is
+// decided).
+template <typename E>
+__device__ __forceinline__ void item_wavefront(const Params& P, const double* e2, int g,
+                                               int lane) {
+  if (g >= P.B * P.nF) return;
+  const int b = g / P.nF;
+  const int f = g - b * P.nF;
+  const unsigned long long a = uniform64(ld_dev(&P.cur.pub[b].a));
+  const unsigned long long c = uniform64(ld_dev(&P.cur.pub[b].c));
+  if (!draw_ready(a, c)) return;       // no draw for this sequence (greedy or invalid)
+  const Draw w = make_draw(P, b, a, c, e2);
+  ItemRuns<E> tr, dr;
+  tr.load(final_row<E>(P, b, w.j, false), f * kItemElems<E>, P.V, lane);
+  if (w.residual) dr.load(final_row<E>(P, b, w.j, true), f * kItemElems<E>, P.V, lane);
+  item_sums<E>(P, b, f, w, tr, dr, lane);
+}
+
+// Pick wavefront of sequence b, after every item is stored.
+template <typename E>
+__device__ __forceinline__ void pick_wavefront(const Params& P, const double* e2, int b, int lane) {
+  if (b >= P.B) return;
+  const unsigned long long a = uniform64(ld_dev(&P.cur.pub[b].a));
+  const unsigned long long c = uniform64(ld_dev(&P.cur.pub[b].c));
+  if (!draw_ready(a, c)) return;
+  wave_pick<E>(P, b, make_draw(P, b, a, c, e2), lane);
+}
+
+// Clears the next call's counters (spread over the pick workgroups).
+__device__ inline void clear_next(const Params& P, int wid, int tid) {
+  const long long stride = (long long)P.n_pick * kThreads;
+  const long long me = (long long)wid * kThreads + tid;
+  for (long long i = me; i < P.B; i += stride) {
+    P.nxt.st[i] = 0ull;
+    P.nxt.pub[i].a = 0ull;
+    P.nxt.pub[i].c = 0ull;
+  }
+  const long long npc = (long long)P.B * (P.D + 1);
+  for (long long i = me; i < npc; i += stride) P.nxt.pc[i] = 0u;
+}
+
+// ------------------------------------------------------------------------------------------
+// the kernels
+
+// Row kernel: one workgroup per row chunk.
 template <typename E>
 __global__ __launch_bounds__(kThreads) void row_kernel(Params P) {
   __shared__ Shared sm;
-  row_workgroup<E>(P, sm, (long long)blockIdx.x, threadIdx.x);
+  row_workgroup<E>(P, sm, int(blockIdx.x), threadIdx.x);
 }
 
-// Final-draw kernel: persistent worker workgroups (four worker wavefronts each).
+// Final-draw kernels, after the row kernel: partial sums (one wavefront per item), then the
+// pick (one wavefront per sequence), which also clears the next call's counters.
 template <typename E>
-__global__ __launch_bounds__(kThreads) void final_kernel(Params P) {
-  __shared__ Shared sm;
-  worker<E>(P, sm, int(blockIdx.x), threadIdx.x);
+__global__ __launch_bounds__(kThreads) void item_kernel(Params P) {
+  __shared__ double e2[256];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 256; i += kThreads) e2[i] = exp2(double(i) / 256.0);
+  __syncthreads();
+  item_wavefront<E>(P, e2, int(blockIdx.x) * kWaves + (tid >> 6), tid & 63);
 }
 
-// Clears the counter region (when a workspace meets a new B or D).
+template <typename E>
+__global__ __launch_bounds__(kThreads) void pick_kernel(Params P) {
+  __shared__ double e2[256];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 256; i += kThreads) e2[i] = exp2(double(i) / 256.0);
+  __syncthreads();
+  pick_wavefront<E>(P, e2, int(blockIdx.x) * kWaves + (tid >> 6), tid & 63);
+  clear_next(P, int(blockIdx.x), tid);
+}
+
+// Clears the counter region (when a workspace meets a new layout).
 __global__ void clear_kernel(unsigned* p, long long n) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -976,52 +995,52 @@ __global__ void clear_kernel(unsigned* p, long long n) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace: [counter set 0][counter set 1] [row partials][position info][descriptors]
-//            [final-draw partials][pick scratch]. A counter set is [Hdr][st B][pc B(D+1)]
-//            [fdone B][qs B]; both sets must be zero when a workspace is first used.
+// Final-draw item length for a dtype: kItemsPerChunk items per row chunk, so that the
+// wavefronts of one position's row workgroups (kWaves per workgroup, 2 * nchunk workgroups per
+// sequence) outnumber the items of the whole batch.
+inline int item_elems(int elem_bytes) { return kRowChunkBytes / elem_bytes / kItemsPerChunk; }
+
+// Workspace: [counter set 0][counter set 1] [row partials][position info]
+//            [final-draw partials][pick scratch]. A counter set is [st B][pc B(D+1)][pub B];
+//            both sets must be zero when a workspace is first used. One layout serves both
+//            dtypes (nF and nchunk are those of the dtype with more).
 struct Layout {
-  int rch, nchunk, nF;
-  size_t set_bytes, off_st, off_pc, off_fdone, off_qs;   // within a counter set
-  size_t off_rpart, off_pinfo, off_desc, off_fpart, off_fmass, total;
+  int nchunk, nF;
+  size_t set_bytes, off_st, off_pc, off_pub;   // within a counter set
+  size_t off_rpart, off_pinfo, off_fpart, off_fmass, total;
 };
 
-inline bool make_layout(int B, int D, int V, int elem_bytes, Layout& L) {
+inline bool make_layout(int B, int D, int V, Layout& L) {
   if (B <= 0 || D < 0 || V <= 0 || D > SV_MAX_D) return false;
-  L.rch = kRowChunkBytes / elem_bytes;
-  L.nchunk = int((size_t(V) + L.rch - 1) / L.rch);
-  L.nF = int((size_t(V) + kMinFinChunk - 1) / kMinFinChunk);   // most items a row can need
-  size_t o = align256(sizeof(Hdr));
+  const int rch = kRowChunkBytes / 4, fch = item_elems(4);      // fp32: the most chunks/items
+  L.nchunk = int((size_t(V) + rch - 1) / rch);
+  L.nF = int((size_t(V) + fch - 1) / fch);
+  size_t o = 0;
   L.off_st = o;    o += align256(size_t(B) * 8);
   L.off_pc = o;    o += align256(size_t(B) * (D + 1) * 4);
-  L.off_fdone = o; o += align256(size_t(B) * 4);
-  L.off_qs = o;    o += align256(size_t(B) * 4);
+  L.off_pub = o;   o += align256(size_t(B) * sizeof(SeqPub));
   L.set_bytes = o;
   o = 2 * L.set_bytes;
   const size_t R = size_t(2) * D + 1;
   L.off_rpart = o; o += align256(size_t(B) * R * L.nchunk * sizeof(RowPart));
   L.off_pinfo = o; o += align256(size_t(B) * (D + 1) * sizeof(PosInfo));
-  L.off_desc = o;  o += align256(size_t(B) * sizeof(SeqDesc));
   L.off_fpart = o; o += align256(size_t(B) * L.nF * sizeof(FinPart));
   L.off_fmass = o; o += align256(size_t(B) * L.nF * sizeof(double));
   L.total = o;
   return true;
 }
 
-// Workspace bytes: the larger of the two dtypes' layouts, so one size serves both.
 inline size_t workspace_bytes(int B, int D, int V) {
-  Layout a, b;
-  if (!make_layout(B, D, V, 2, a) || !make_layout(B, D, V, 4, b)) return 0;
-  return a.total > b.total ? a.total : b.total;
+  Layout a;
+  return make_layout(B, D, V, a) ? a.total : 0;
 }
 
 inline CounterSet counter_set(char* base, const Layout& L, int k) {
   char* s = base + size_t(k) * L.set_bytes;
   CounterSet c;
-  c.hdr = reinterpret_cast<Hdr*>(s);
   c.st = reinterpret_cast<unsigned long long*>(s + L.off_st);
   c.pc = reinterpret_cast<unsigned*>(s + L.off_pc);
-  c.fdone = reinterpret_cast<unsigned*>(s + L.off_fdone);
-  c.qs = reinterpret_cast<unsigned*>(s + L.off_qs);
+  c.pub = reinterpret_cast<SeqPub*>(s + L.off_pub);
   return c;
 }
 
@@ -1032,7 +1051,7 @@ struct DeviceWorkspace {
 
 struct WsState {      // host-side knowledge about one workspace
   long long calls = 0;        // calls made with it (the parity picks the counter set)
-  int B = -1, D = -1;         // counter layout of the last call (-1: zero-filled, unused)
+  int B = -1, D = -1, V = -1; // layout of the last call (-1: zero-filled, unused)
 };
 
 std::mutex g_ws_mutex;
@@ -1047,32 +1066,6 @@ struct Profile {        // optional timing of the kernel: one event pair per cal
 std::mutex g_prof_mutex;
 Profile g_prof;
 
-std::mutex g_dev_mutex;
-std::map<int, int> g_cus;        // device -> compute units
-
-// A second stream per (device, caller stream) for the final-draw workers, with the two events
-// that fork it from and join it back to the caller's stream. Default priority.
-struct Side {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-std::mutex g_side_mutex;
-std::map<std::pair<int, hipStream_t>, Side> g_side;
-
-Side* side_stream(hipStream_t caller) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  std::lock_guard<std::mutex> lk(g_side_mutex);
-  Side& sd = g_side[{dev, caller}];
-  if (!sd.s) {
-    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess) { sd.s = nullptr; return nullptr; }
-    if (hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess)
-      return nullptr;
-  }
-  return &sd;
-}
-
 int check_args(const void* t, const void* d, const int32_t* tok, const float* u, const float* temp,
                int32_t* ol, int32_t* ot, int B, int D, int V) {
   if (B <= 0 || D < 0 || V <= 0 || D > SV_MAX_D) return SV_EINVAL;
@@ -1083,35 +1076,13 @@ int check_args(const void* t, const void* d, const int32_t* tok, const float* u,
   return SV_OK;
 }
 
-int compute_units(int dev) {
-  std::lock_guard<std::mutex> lk(g_dev_mutex);
-  auto it = g_cus.find(dev);
-  if (it != g_cus.end()) return it->second;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return -1;
-  g_cus[dev] = cus;
-  return cus;
-}
-
 template <typename E>
-int launch(Params& P, int dev, hipStream_t stream) {
-  const int cus = compute_units(dev);
-  if (cus <= 0) return SV_EHIP;
-  // Worker wavefronts: four per workgroup, kWorkersPerCU workgroups per CU. Items are sized so
-  // each worker wavefront gets about four: small items keep the work after the last decision
-  // short, large ones keep the per-item overhead low when there are many draws.
-  const long long waves = 4ll * kWorkersPerCU * cus;
-  long long fch = ((long long)P.B * P.V + 4 * waves - 1) / (4 * waves);
-  fch = (fch + 511) / 512 * 512;
-  fch = fch < kMinFinChunk ? kMinFinChunk : (fch > kMaxFinChunk ? kMaxFinChunk : fch);
-  P.fch = int(fch);
-  P.nF = int((P.V + fch - 1) / fch);
-  const long long items = (long long)P.B * P.nF;
-  const long long wg = (items + 3) / 4;
-  P.n_workers = int(wg < (long long)kWorkersPerCU * cus ? wg : (long long)kWorkersPerCU * cus);
+int launch(Params& P, hipStream_t stream) {
   const long long rows = (long long)(P.D + 1) * P.B * 2 * P.nchunk;
-  if (rows > 0x7fffffffll) return SV_EINVAL;
+  const long long items = ((long long)P.B * P.nF + kWaves - 1) / kWaves;
+  const long long picks = ((long long)P.B + kWaves - 1) / kWaves;
+  if (rows > 0x7fffffffll || items > 0x7fffffffll) return SV_EINVAL;
+  P.n_pick = int(picks);
 
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   {
@@ -1122,28 +1093,13 @@ int launch(Params& P, int dev, hipStream_t stream) {
       ++g_prof.used;
     }
   }
-  if (kConcurrent) {
-    // the final-draw workers run alongside the row kernel on a second stream: fork after the
-    // caller's earlier work, join before the caller's later work
-    Side* side = side_stream(stream);
-    if (!side) return SV_EHIP;
-    if (hipEventRecord(side->fork, stream) != hipSuccess) return SV_EHIP;
-    if (hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess) return SV_EHIP;
-    hipLaunchKernelGGL(final_kernel<E>, dim3(unsigned(P.n_workers)), dim3(kThreads), 0, side->s, P);
-    if (hipGetLastError() != hipSuccess) return SV_EHIP;
-    if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return SV_EHIP;
-    hipLaunchKernelGGL(row_kernel<E>, dim3(unsigned(rows)), dim3(kThreads), 0, stream, P);
-    if (hipGetLastError() != hipSuccess) return SV_EHIP;
-    if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return SV_EHIP;
-    if (hipEventRecord(side->join, side->s) != hipSuccess) return SV_EHIP;
-    if (hipStreamWaitEvent(stream, side->join, 0) != hipSuccess) return SV_EHIP;
-    return SV_OK;
-  }
   if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return SV_EHIP;
   hipLaunchKernelGGL(row_kernel<E>, dim3(unsigned(rows)), dim3(kThreads), 0, stream, P);
   if (hipGetLastError() != hipSuccess) return SV_EHIP;
   if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return SV_EHIP;
-  hipLaunchKernelGGL(final_kernel<E>, dim3(unsigned(P.n_workers)), dim3(kThreads), 0, stream, P);
+  hipLaunchKernelGGL(item_kernel<E>, dim3(unsigned(items)), dim3(kThreads), 0, stream, P);
+  if (hipGetLastError() != hipSuccess) return SV_EHIP;
+  hipLaunchKernelGGL(pick_kernel<E>, dim3(unsigned(picks)), dim3(kThreads), 0, stream, P);
   if (hipGetLastError() != hipSuccess) return SV_EHIP;
   return SV_OK;
 }
@@ -1156,7 +1112,8 @@ int run(int dtype, const void* target, const void* draft, const int32_t* tokens,
   int rc = check_args(target, draft, tokens, uniforms, temperature, out_len, out_tokens, B, D, V);
   if (rc != SV_OK) return rc;
   Layout lay;
-  make_layout(B, D, V, dtype == 1 ? 2 : 4, lay);
+  make_layout(B, D, V, lay);
+  const int elem_bytes = dtype == 1 ? 2 : 4;
   const size_t need = workspace_bytes(B, D, V);
   if (ws != nullptr && (ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255)))
     return SV_ENOMEM;
@@ -1185,8 +1142,8 @@ int run(int dtype, const void* target, const void* draft, const int32_t* tokens,
   }
   WsState& state = g_ws_state[ws];
   char* base = static_cast<char*>(ws);
-  if (state.B >= 0 && (state.B != B || state.D != D)) {
-    // the counter layout changed: clear both counter sets (a small kernel, graph-safe)
+  if (state.B >= 0 && (state.B != B || state.D != D || state.V != V)) {
+    // the layout changed: clear both counter sets (a small kernel, graph-safe)
     const long long n = (long long)(2 * lay.set_bytes / 4);
     hipLaunchKernelGGL(clear_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream,
                        reinterpret_cast<unsigned*>(base), n);
@@ -1194,6 +1151,7 @@ int run(int dtype, const void* target, const void* draft, const int32_t* tokens,
   }
   state.B = B;
   state.D = D;
+  state.V = V;
   const int parity = int(state.calls & 1);
   ++state.calls;
 
@@ -1210,13 +1168,14 @@ int run(int dtype, const void* target, const void* draft, const int32_t* tokens,
   P.D = D;
   P.V = V;
   P.R = 2 * D + 1;
-  P.rch = lay.rch;
-  P.nchunk = lay.nchunk;
+  P.rch = kRowChunkBytes / elem_bytes;
+  P.nchunk = int((size_t(V) + P.rch - 1) / P.rch);
+  P.fch = item_elems(elem_bytes);
+  P.nF = int((size_t(V) + P.fch - 1) / P.fch);
   P.cur = counter_set(base, lay, parity);
   P.nxt = counter_set(base, lay, 1 - parity);
   P.rpart = reinterpret_cast<RowPart*>(base + lay.off_rpart);
   P.pinfo = reinterpret_cast<PosInfo*>(base + lay.off_pinfo);
-  P.desc = reinterpret_cast<SeqDesc*>(base + lay.off_desc);
   P.fpart = reinterpret_cast<FinPart*>(base + lay.off_fpart);
   P.fmass = reinterpret_cast<double*>(base + lay.off_fmass);
   P.dbg_row_stats = dbg_stats;
@@ -1228,7 +1187,7 @@ int run(int dtype, const void* target, const void* draft, const int32_t* tokens,
     return SV_EHIP;                    // -1
   if (dbg_logpq && D > 0 && hipMemsetAsync(dbg_logpq, 0xff, size_t(B) * D * 2 * 4, stream) != hipSuccess)
     return SV_EHIP;
-  return dtype == 1 ? launch<uint16_t>(P, dev, stream) : launch<float>(P, dev, stream);
+  return dtype == 1 ? launch<uint16_t>(P, stream) : launch<float>(P, stream);
 }
 
 }  // namespace sv
