@@ -88,11 +88,15 @@ struct SeqPub {
                           // marker; moves the estimate by one ulp, far inside the band)
 };
 
+constexpr int kMaxItemBlocks = 4;
+
 struct FinPart {      // fp64 sums of one final-draw item
   double st, sd;      // sum e_t, sum e_d   (e = exp((x - max) / T))
   double at, ad;      // sums over elements certainly in the positive part of p - q
   double bt, bd;      // sums over the elements inside the band
   double dmin, dmax;  // min / max of x_t - x_d inside the band (+inf / -inf: none)
+  double kat[kMaxItemBlocks], kad[kMaxItemBlocks];   // at, ad of each 512-element block
+                                                     // (bonus draws: kat = e_t per block)
 };
 
 struct CounterSet {   // everything that must be zero when a call starts
@@ -203,6 +207,14 @@ template <> struct Run<uint16_t> {
   __device__ unsigned bits(int e) const {
     return (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu);
   }
+  // a copy whose values the compiler cannot equate with this one's (no common subexpressions
+  // kept alive across a long stretch of code)
+  __device__ Run opaque() const {
+    Run r = *this;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(r.w[k]));
+    return r;
+  }
 };
 template <> struct Run<float> {
   float x[kFinPer];
@@ -219,6 +231,12 @@ template <> struct Run<float> {
     }
   }
   __device__ float at(int e) const { return x[e]; }
+  __device__ Run opaque() const {
+    Run r = *this;
+#pragma unroll
+    for (int e = 0; e < kFinPer; ++e) asm volatile("" : "+v"(r.x[e]));
+    return r;
+  }
 };
 
 // wave-uniform values kept in scalar registers
@@ -284,6 +302,45 @@ __device__ inline void wave_am(float& v, int& i) {
     const int i2 = __shfl_xor(i, off);
     am_combine(v, i, v2, i2);
   }
+}
+
+// Inclusive scans of a double over the 64 lanes with DPP row shifts and row broadcasts (VALU
+// only, no LDS traffic): Hillis-Steele within rows of 16, then row 0's total into row 1 and
+// row 2's into row 3, then the total of rows 0-1 into rows 2 and 3. Lane 63 ends with the
+// reduction of all lanes. Lanes a shift reads from outside the row contribute `id` (the
+// operation's identity).
+template <int CTRL, int ROWS>
+__device__ inline double dpp_double(double x, double id) {
+  const int lo = __builtin_amdgcn_update_dpp(__double2loint(id), __double2loint(x), CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(__double2hiint(id), __double2hiint(x), CTRL, ROWS, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
+template <typename Op>
+__device__ inline double dpp_scan(double x, double id, Op op) {
+  x = op(x, dpp_double<0x111, 0xf>(x, id));   // row_shr:1
+  x = op(x, dpp_double<0x112, 0xf>(x, id));   // row_shr:2
+  x = op(x, dpp_double<0x114, 0xf>(x, id));   // row_shr:4
+  x = op(x, dpp_double<0x118, 0xf>(x, id));   // row_shr:8
+  x = op(x, dpp_double<0x142, 0xa>(x, id));   // row_bcast:15 into rows 1 and 3
+  x = op(x, dpp_double<0x143, 0xc>(x, id));   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+__device__ inline double dpp_scan_add(double x) {
+  return dpp_scan(x, 0.0, [](double u, double v) { return u + v; });
+}
+// value of lane l (wave-uniform l)
+__device__ inline double readlane(double x, int l) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(x), l),
+                          __builtin_amdgcn_readlane(__double2loint(x), l));
+}
+// sum over the wavefront, in every lane
+__device__ inline double wave_total(double x) { return readlane(dpp_scan_add(x), 63); }
+// lane i gets lane i - 1's x, lane 0 gets first
+__device__ inline double lane_before(double x, double first) {
+  const int lo = __builtin_amdgcn_update_dpp(__double2loint(first), __double2loint(x), 0x138, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(__double2hiint(first), __double2hiint(x), 0x138, 0xf, 0xf, false);
+  return __hiloint2double(hi, lo);
 }
 
 __device__ inline double wave_sum(double x) {
@@ -638,16 +695,6 @@ __device__ inline double exact_weight(const Run<E>& rt, const Run<E>& rd, int e,
   return fmax(0.0, et * it - ed * id);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wavefront.
-__device__ inline double wave_inclusive_scan(double x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  return x;
-}
-
 // Sum of the exact weights of one item's elements (fixed order); target_only as above. Only
 // for the rare sequences whose band did not resolve every element.
 template <typename E>
@@ -707,8 +754,8 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
     sd += x.sd;
     if (x.dmin < x.dmax) multi = 1;
   }
-  st = wave_sum(st);
-  sd = wave_sum(sd);
+  st = wave_total(st);
+  sd = wave_total(sd);
   const double it = 1.0 / st, id = 1.0 / sd;
   // did the band hold the exact ratio (with room for the rounding of its bounds), and is every
   // item's in-band set one ratio class?
@@ -735,11 +782,11 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
   // Z, then the first item whose inclusive prefix exceeds t = u Z (else the last item with
   // positive mass), 64 items at a time
   double Z = 0.0;
-  for (int base = 0; base < nF; base += 64) Z += wave_sum(mass(base + lane));
+  for (int base = 0; base < nF; base += 64) Z += wave_total(mass(base + lane));
   if (!(Z > 0.0) && !target_only) {
     target_only = true;                // residual of zero mass (rounding only): draw from p_j
     Z = 0.0;
-    for (int base = 0; base < nF; base += 64) Z += wave_sum(mass(base + lane));
+    for (int base = 0; base < nF; base += 64) Z += wave_total(mass(base + lane));
   }
   const double t = w.u * Z;
   int fstar = -1, flast = -1;
@@ -747,16 +794,16 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
   for (int base = 0; base < nF && fstar < 0; base += 64) {
     const int f = base + lane;
     const double m = mass(f);
-    const double inc = wave_inclusive_scan(m, lane) + total;
+    const double inc = dpp_scan_add(m) + total;
     const unsigned long long over = __ballot(f < nF && inc > t);
     const unsigned long long pos = __ballot(f < nF && m > 0.0);
     if (pos) flast = base + 63 - __builtin_clzll(pos);
     if (over) {
       const int l = __builtin_ctzll(over);
       fstar = base + l;
-      run = __shfl(inc - m, l);
+      run = readlane(inc - m, l);
     }
-    total = __shfl(inc, 63);
+    total = readlane(inc, 63);
   }
   const bool past_end = fstar < 0;
   int32_t* out = P.out_tokens + size_t(b) * (P.D + 1) + w.j;
@@ -768,32 +815,50 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
     }
   }
 
-  // rescan the chosen item block by block, in ascending element order
+  // The chosen item's elements. Its block masses come from the item record when they can (no
+  // in-band element, and the draw's weights are the ones the blocks summed); then only the block
+  // holding t is rescanned, else every block in order.
   const int a0 = fstar * kItemElems<E>;
   ItemRuns<E> tr, dr;
   tr.load(trow, a0, P.V, lane);
   if (!target_only) dr.load(drow, a0, P.V, lane);
+  constexpr int KB = kItemBlocks<E>;
+  const FinPart* rf = fp + fstar;
+  const bool bonus = !w.residual;
+  const bool blockwise = !past_end && !slow && (bonus || (!target_only &&
+                         !(ld_dev(&rf->dmin) <= ld_dev(&rf->dmax))));
+  int kfirst = 0, klast = KB - 1;
+  if (blockwise) {
+    double bm = 0.0;                   // lane k: mass of block k
+    if (lane < KB) {
+      const double ka = ld_dev(&rf->kat[lane]);
+      bm = bonus ? ka : fmax(0.0, ka * it - ld_dev(&rf->kad[lane]) * id);
+    }
+    const double inc = dpp_scan_add(bm) + run;
+    const unsigned long long over = __ballot(lane < KB && inc > t);
+    if (over) {                        // else rounding: rescan every block
+      kfirst = klast = __builtin_ctzll(over);
+      run = readlane(inc - bm, kfirst);
+    }
+  }
   int found = -1, last_pos = -1;
 #pragma unroll
-  for (int k = 0; k < kItemBlocks<E>; ++k) {
-    if (found < 0) {                   // wave-uniform
+  for (int k = 0; k < KB; ++k) {
+    if (found < 0 && k >= kfirst && k <= klast) {     // wave-uniform
       const int a = a0 + kFinBlock * k + kFinPer * lane;
       const int n = max(0, min(kFinPer, P.V - a));
       double ls = 0.0;
-      int my_last = -1;
 #pragma unroll
       for (int e = 0; e < kFinPer; ++e) {
         if (e < n) {
           const double wt = exact_weight<E>(tr.r[k], dr.r[k], e, w, target_only, it, id);
           ls += wt;
-          if (wt > 0.0) my_last = a + e;
+          if (wt > 0.0) last_pos = a + e;
         }
       }
-      const double inc = wave_inclusive_scan(ls, lane) + run;
+      const double inc = dpp_scan_add(ls) + run;
       // lane l owns [prefix before l, prefix through l): consecutive stored values, one owner
-      const double lo = __shfl_up(inc, 1);
-      const double mylo = (lane == 0) ? run : lo;
-      last_pos = max(last_pos, my_last);
+      const double mylo = lane_before(inc, run);
       const bool owner = !past_end && ls > 0.0 && mylo <= t && t < inc;
       const unsigned long long own = __ballot(owner);
       if (own) {
@@ -801,18 +866,21 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
         int k2 = -1;
         if (lane == ol) {
           double acc = mylo;
+          int my_last = -1;
 #pragma unroll
           for (int e = 0; e < kFinPer; ++e) {
             if (e < n && k2 < 0) {
-              acc += exact_weight<E>(tr.r[k], dr.r[k], e, w, target_only, it, id);
+              const double wt = exact_weight<E>(tr.r[k], dr.r[k], e, w, target_only, it, id);
+              acc += wt;
+              if (wt > 0.0) my_last = a + e;
               if (acc > t) k2 = a + e;
             }
           }
-          if (k2 < 0) k2 = my_last;
+          if (k2 < 0) k2 = my_last;    // rounding: the lane's last element of positive weight
         }
-        found = __shfl(k2, ol);
+        found = __builtin_amdgcn_readlane(k2, ol);
       }
-      run = __shfl(inc, 63);
+      run = readlane(inc, 63);
     }
   }
   // rounding put u * Z past the end: the last element with positive weight
@@ -820,52 +888,117 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
   if (lane == 0) *out = (found >= 0) ? found : last_pos;
 }
 
+// Main sweep of an item: per block, the sum of e_t (bonus draws) or the sums of e_t and e_d
+// over the elements above the band (residual draws, which also sum e_t and e_d over all
+// elements); returns whether any of the lane's elements lies inside the band.
+// FULL: every element of the item exists (all items but a row's last).
+template <typename E, bool FULL, bool RES>
+__device__ __forceinline__ bool item_sweep(const Params& P, int a0, const Draw& w,
+                                           const ItemRuns<E>& tr, const ItemRuns<E>& dr,
+                                           int lane, double& st, double& sd, double* kat,
+                                           double* kad) {
+  int band = 0;
+#pragma unroll
+  for (int k = 0; k < kItemBlocks<E>; ++k) {
+    const int n = FULL ? kFinPer : max(0, min(kFinPer, P.V - (a0 + kFinBlock * k + kFinPer * lane)));
+#pragma unroll
+    for (int e = 0; e < kFinPer; ++e) {
+      if (FULL || e < n) {
+        const double xt = tr.r[k].at(e);
+        const double et = w.t(float(xt));
+        if (RES) {
+          st += et;
+          const double xd = dr.r[k].at(e);
+          const double ed = w.d(float(xd));
+          sd += ed;
+          // x_t - x_d against the band: above it the element is certainly in the positive part
+          const double dx = xt - xd;
+          const double above = dx > w.dhi ? 1.0 : 0.0;
+          kat[k] = fma(above, et, kat[k]);
+          kad[k] = fma(above, ed, kad[k]);
+          band |= int(dx <= w.dhi) & int(dx >= w.dlo);     // no branch per element
+        } else {
+          kat[k] += et;
+        }
+      }
+    }
+  }
+  return band != 0;
+}
+
 // fp64 partial sums of item f of sequence b from the lane's runs, stored to the item's record
-// (no wait).
+// (no wait). The rare elements inside the band are summed by a second sweep, taken only by
+// wavefronts that have some.
 template <typename E>
 __device__ __forceinline__ void item_sums(const Params& P, int b, int f, const Draw& w,
                                           const ItemRuns<E>& tr, const ItemRuns<E>& dr,
                                           int lane) {
+  constexpr int KB = kItemBlocks<E>;
   const int a0 = f * kItemElems<E>;
-  double st = 0, sd = 0, at = 0, ad = 0, bt = 0, bd = 0, dmin = INFINITY, dmax = -INFINITY;
+  const bool full = a0 + kItemElems<E> <= P.V;
+  double st = 0, sd = 0, bt = 0, bd = 0, dmin = INFINITY, dmax = -INFINITY;
+  double kat[KB], kad[KB];
 #pragma unroll
-  for (int k = 0; k < kItemBlocks<E>; ++k) {
-    const int n = max(0, min(kFinPer, P.V - (a0 + kFinBlock * k + kFinPer * lane)));
-#pragma unroll
-    for (int e = 0; e < kFinPer; ++e) {
-      if (e >= n) continue;
-      const double et = w.t(tr.r[k].at(e));
-      st += et;
-      if (w.residual) {
-        const double ed = w.d(dr.r[k].at(e));
-        sd += ed;
-        // x_t - x_d against the band: above it the element is certainly in the positive part
-        const double dx = double(tr.r[k].at(e)) - double(dr.r[k].at(e));
-        const double above = dx > w.dhi ? 1.0 : 0.0;
-        at = fma(above, et, at);
-        ad = fma(above, ed, ad);
-        if (dx <= w.dhi && dx >= w.dlo) {              // inside the band (rare)
-          bt += et;
-          bd += ed;
+  for (int k = 0; k < KB; ++k) kat[k] = kad[k] = 0.0;
+  bool band;
+  if (w.residual) {
+    band = full ? item_sweep<E, true, true>(P, a0, w, tr, dr, lane, st, sd, kat, kad)
+                : item_sweep<E, false, true>(P, a0, w, tr, dr, lane, st, sd, kat, kad);
+  } else {
+    band = full ? item_sweep<E, true, false>(P, a0, w, tr, dr, lane, st, sd, kat, kad)
+                : item_sweep<E, false, false>(P, a0, w, tr, dr, lane, st, sd, kat, kad);
+  }
+  if (__any(band)) {                   // rare: reload the item and sum its in-band elements
+    const E* trow = final_row<E>(P, b, w.j, false);
+    const E* drow = final_row<E>(P, b, w.j, true);
+    for (int k = 0; k < KB; ++k) {
+      const int a = a0 + kFinBlock * k + kFinPer * lane;
+      const int n = max(0, min(kFinPer, P.V - a));
+      for (int e = 0; e < n; ++e) {
+        const double xt = Elem<E>::get(trow, size_t(a + e));
+        const double xd = Elem<E>::get(drow, size_t(a + e));
+        const double dx = xt - xd;
+        if (dx <= w.dhi && dx >= w.dlo) {
+          bt += w.t(float(xt));
+          bd += w.d(float(xd));
           dmin = fmin(dmin, dx);
           dmax = fmax(dmax, dx);
         }
       }
     }
   }
-  st = wave_sum(st);
-  sd = wave_sum(sd);
-  at = wave_sum(at);
-  ad = wave_sum(ad);
-  bt = wave_sum(bt);
-  bd = wave_sum(bd);
-  dmin = wave_min(dmin);
-  dmax = wave_max(dmax);
-  // every lane holds the same totals (butterfly reductions); lane k stores field k
-  if (lane < 8) {
-    const double v = lane == 0 ? st : lane == 1 ? sd : lane == 2 ? at : lane == 3 ? ad
-                   : lane == 4 ? bt : lane == 5 ? bd : lane == 6 ? dmin : dmax;
-    st_dev(reinterpret_cast<double*>(P.fpart + size_t(b) * P.nF + f) + lane, v);
+  const auto add = [](double u, double v) { return u + v; };
+  const auto mn = [](double u, double v) { return fmin(u, v); };
+  const auto mx = [](double u, double v) { return fmax(u, v); };
+#pragma unroll
+  for (int k = 0; k < KB; ++k) {
+    kat[k] = dpp_scan(kat[k], 0.0, add);
+    if (w.residual) kad[k] = dpp_scan(kad[k], 0.0, add);
+  }
+  if (w.residual) {
+    st = dpp_scan(st, 0.0, add);
+    sd = dpp_scan(sd, 0.0, add);
+    bt = dpp_scan(bt, 0.0, add);
+    bd = dpp_scan(bd, 0.0, add);
+    dmin = dpp_scan(dmin, INFINITY, mn);
+    dmax = dpp_scan(dmax, -INFINITY, mx);
+  }
+  if (lane == 63) {                    // plain stores: the pick kernel runs after this kernel
+    double at = 0.0, ad = 0.0, et = 0.0;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      at += kat[k];
+      ad += kad[k];
+    }
+    if (!w.residual) et = at;          // bonus draw: the block sums are sums of e_t
+    FinPart* q = P.fpart + size_t(b) * P.nF + f;
+    q->st = w.residual ? st : et; q->sd = sd; q->at = at; q->ad = ad;
+    q->bt = bt; q->bd = bd; q->dmin = dmin; q->dmax = dmax;
+#pragma unroll
+    for (int k = 0; k < kMaxItemBlocks; ++k) {
+      q->kat[k] = k < KB ? kat[k] : 0.0;
+      q->kad[k] = k < KB ? kad[k] : 0.0;
+    }
   }
 }
 
