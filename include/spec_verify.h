@@ -92,10 +92,9 @@ size_t spec_verify_workspace_bytes(int B, int D, int V);
 
 /* Same operation with caller-provided device workspace of at least
  * spec_verify_workspace_bytes(B, D, V) bytes, 256-byte aligned. dtype: 0 = fp32, 1 = bf16.
- * Nothing is allocated. The workspace must be zero-filled before its first use; every call
- * leaves the parts later calls rely on zeroed again (when a later call has a larger B, the
- * library clears the extra counter slots itself, with a small kernel on `stream`). It must not
- * be used by another call until this call's stream work has completed. */
+ * Nothing is allocated. The workspace needs no initialisation (each call writes every part
+ * it reads) and must not be used by another call until this call's stream work has
+ * completed. */
 int spec_verify_ws(int dtype, const void* target_logits, const void* draft_logits,
                    const int32_t* draft_tokens, const int32_t* draft_lens,
                    const float* uniforms, int B, int D, int V,

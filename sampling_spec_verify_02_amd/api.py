@@ -68,8 +68,8 @@ def spec_verify(target_logits, draft_logits, draft_tokens, draft_lens, uniforms,
     target_logits [B][D+1][V] and draft_logits [B][D][V]: bfloat16 or float32 (same dtype);
     draft_tokens [B][D] int32; draft_lens [B] int32 or None (all D); uniforms [B][D+1] float32;
     temperature: [B] float32 tensor or a Python float. workspace: optional uint8 GPU tensor of
-    at least workspace_bytes(B, D, V) bytes, zero-filled before its first use (torch.zeros);
-    the library's own buffer is used otherwise.
+    at least workspace_bytes(B, D, V) bytes (no initialisation needed); the library's own
+    buffer is used otherwise.
     The work is enqueued on torch's current stream; nothing is synchronised."""
     B, D, V, temperature, out_accept_len, out_tokens = _prepare(
         target_logits, draft_logits, draft_tokens, draft_lens, uniforms, temperature,

@@ -6,35 +6,29 @@
 // spéculatif"), in-order acceptance up to the first mismatch and AL in [1, 1 + D] from
 // "NVIDIA: öt irányelv ..." (section "Mit csinál a spekulatív dekódolás?").
 //
-// Three kernels per call, in stream order.
+// Three kernels per call, in stream order; each hands its results to the next through the
+// kernel boundary, so no kernel waits for another workgroup and none uses atomics.
 //
 // * Row kernel: one workgroup per 32 KB chunk of a row, position-major order (all position-0
 //   rows of the batch first, then position 1, ...). It streams its chunk with non-temporal
-//   16-byte loads and produces the chunk's exact max and fp32 sum exp((x - max) / T) (sampled
+//   16-byte loads and stores the chunk's exact max and fp32 sum exp((x - max) / T) (sampled
 //   rows) or max and lowest argmax (greedy target rows); the chunk holding the draft token x_p
 //   also records the logit at x_p. Rows the method does not need (padding, draft rows of greedy
-//   sequences) are not read. The workgroup completing the last chunk of a (sequence, position)
-//   pair evaluates that position's test, u_p < min(1, p_p(x_p)/q_p(x_p)) (or x_p == argmax for
-//   greedy), and ORs "position p done" and "position p rejects" into the sequence's 64-bit
-//   state word. The outcome is decided once a rejection is preceded by a complete prefix of
-//   evaluated positions, or once positions 0..L are all done without one; exactly one OR makes
-//   that transition, and its wavefront writes the accepted tokens and AL and publishes the
-//   sequence's final-draw descriptor. No workgroup ever waits for another.
-// * Item kernel: one wavefront per final-draw item (b, f), kItemElems consecutive elements of
-//   sequence b's final row(s) (target and draft row j after a rejection at j, target row L for
-//   the bonus draw). It forms fp64 normalising sums and the residual mass linearised around the
-//   fp32 estimate rho~ of rho = S_t / S_d: elements whose x_t - x_d puts ln(e_t / e_d) clearly
-//   above ln rho~ are certainly in the positive part of p - q and contribute e_t / S_t - e_d /
-//   S_d, those clearly below contribute nothing, those inside the band are summed apart with
-//   the range of their x_t - x_d (one value means one exact ratio class, resolved exactly by
-//   the pick).
+//   sequences, rows of invalid sequences) are not read.
+// * Item kernel: one wavefront per final-draw item (b, f). The wavefront first derives sequence
+//   b's outcome from the row partials: per-row statistics by a fixed combine tree, the test
+//   u_p < min(1, p_p(x_p)/q_p(x_p)) (or x_p == argmax for greedy) at every position, the first
+//   rejection j. Every wavefront of the sequence computes the same bits; item 0's writes the
+//   accepted tokens, AL and the final-draw descriptor. An item covers kItemElems consecutive
+//   elements of the final row(s) (target and draft row j after a rejection at j, target row L
+//   for the bonus draw). It forms fp64 normalising sums and the residual mass linearised around
+//   the fp32 estimate rho~ of rho = S_t / S_d: elements whose x_t - x_d puts ln(e_t / e_d)
+//   clearly above ln rho~ are certainly in the positive part of p - q and contribute
+//   e_t / S_t - e_d / S_d, those clearly below contribute nothing, those inside the band are
+//   summed apart with the range of their x_t - x_d (one value means one exact ratio class,
+//   resolved exactly by the pick).
 // * Pick kernel: one wavefront per sequence. Exact normalisers from the item sums, the item
 //   masses, the item holding u * Z, and an fp64 prefix-scan rescan of that item give the token.
-//   It also clears the counters of the next call.
-//
-// Hand-offs inside the row kernel use device-coherent (sc1) atomic stores and loads and relaxed
-// device-scope atomics: a device-scope release/acquire fence would write back and invalidate
-// the XCD's whole L2 on every hand-off. The counters come in two sets used by alternate calls.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -71,21 +65,14 @@ struct RowPart {      // partial statistics of one row chunk
   float pad;
 };
 
-struct PosInfo {      // what the evaluation of one (sequence, position) found
-  float mt, md;       // exact row maxima (target, draft)
-  float lnrho;        // fp32 ln(S_t / S_d)
-  int g;              // greedy: target argmax
-};
-
-// Outcome of one sequence as published to the final-draw items: two 64-bit words, each
-// written and read in one access. A reader takes the pair only when both are set, so it needs
-// no ordering between them.
+// Outcome of one sequence as handed to the pick kernel: two 64-bit words.
 struct SeqPub {
   unsigned long long a;   // bits 0-1 Mode, 2-6 position j of the final draw, 32-63 bits of
                           // the exact max of target row j
   unsigned long long c;   // bits 0-31 bits of the exact max of draft row j, 32-63 bits of the
-                          // fp32 ln(S_t / S_d) of row j with its lowest bit forced to 1 (set
-                          // marker; moves the estimate by one ulp, far inside the band)
+                          // fp32 ln(S_t / S_d) of row j with its lowest bit forced to 1 (a
+                          // marker that a draw is due; moves the estimate by one ulp, far
+                          // inside the band)
 };
 
 constexpr int kMaxItemBlocks = 4;
@@ -97,12 +84,6 @@ struct FinPart {      // fp64 sums of one final-draw item
   double dmin, dmax;  // min / max of x_t - x_d inside the band (+inf / -inf: none)
   double kat[kMaxItemBlocks], kad[kMaxItemBlocks];   // at, ad of each 512-element block
                                                      // (bonus draws: kat = e_t per block)
-};
-
-struct CounterSet {   // everything that must be zero when a call starts
-  unsigned long long* st;   // [B] done bits 0..31, reject bits 32..63
-  unsigned* pc;             // [B][D+1] completed chunks of the position's rows
-  SeqPub* pub;              // [B] outcome of the sequence (zero until decided)
 };
 
 struct Params {
@@ -120,11 +101,8 @@ struct Params {
   int nchunk;         // row chunks per row
   int fch;            // elements per final-draw item (rch / kItemsPerChunk, a multiple of 512)
   int nF;             // final-draw items per sequence
-  int n_pick;         // pick workgroups (four sequences each; they clear the next counters)
-  CounterSet cur;     // this call's counters
-  CounterSet nxt;     // the next call's counters, cleared by the pick kernel
+  SeqPub* pub;        // [B] outcome of each sequence (item kernel -> pick kernel)
   RowPart* rpart;     // [B][R][nchunk]
-  PosInfo* pinfo;     // [B][D+1]
   FinPart* fpart;     // [B][nF]
   double* fmass;      // [B][nF] scratch of the pick
   float* dbg_row_stats;  // optional [B][R][2]
@@ -133,7 +111,7 @@ struct Params {
 };
 
 // ------------------------------------------------------------------------------------------
-// device-coherent accesses
+// device-coherent accesses (the pick's scratch masses: one lane stores, others load them back)
 
 template <typename T>
 __device__ inline void st_dev(T* p, T v) {
@@ -143,14 +121,8 @@ template <typename T>
 __device__ inline T ld_dev(const T* p) {
   return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline unsigned add_dev(unsigned* p, unsigned v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline unsigned long long or_dev(unsigned long long* p, unsigned long long v) {
-  return __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Wait until this wavefront's earlier vector-memory operations (the device-coherent stores of
-// a result) have completed, before a counter announces them.
+// Wait until this wavefront's earlier vector-memory operations (the stores of the scratch
+// masses) have completed, before they are loaded back.
 __device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ------------------------------------------------------------------------------------------
@@ -252,22 +224,6 @@ __device__ inline bool seq_valid(int L, int D, float T) {
   return L >= 0 && L <= D && isfinite(T) && T >= 0.f;
 }
 
-// chunks of the rows of (sequence, position p) that the method needs
-__device__ inline int pair_chunks(int p, int L, bool greedy, int nchunk) {
-  return (p <= L ? nchunk : 0) + ((!greedy && p < L) ? nchunk : 0);
-}
-
-// Has the outcome been decided by state word w? Sets j (position of the final token).
-__device__ inline bool decided(unsigned long long w, int L, int& j) {
-  const unsigned done = unsigned(w), rej = unsigned(w >> 32);
-  const int k = __builtin_ctz(~done);                 // positions 0..k-1 evaluated
-  const unsigned pre = (k >= 32) ? 0xffffffffu : ((1u << k) - 1u);
-  const unsigned r = rej & pre;
-  if (r) { j = __builtin_ctz(r); return true; }
-  if (k >= L + 1) { j = L; return true; }
-  return false;
-}
-
 // ------------------------------------------------------------------------------------------
 // reductions (fixed trees, so identical inputs give identical bits)
 
@@ -366,136 +322,12 @@ struct Shared {
   float red[kWaves][2];         // cross-wavefront combine of the row chunk
 };
 
-
-
 // ------------------------------------------------------------------------------------------
-// outcome of a sequence (one wavefront of the deciding workgroup)
+// row chunk: statistics of one 32 KB chunk (whole workgroup), stored by wavefront 0
 
 template <typename E>
-__device__ __forceinline__ void decide(const Params& P, int b, int L, float T, bool greedy, int j, int lane) {
-  const int D = P.D;
-  const int32_t* xs = P.tokens + size_t(b) * D;
-  int32_t* toks = P.out_tokens + size_t(b) * (D + 1);
-  const bool bad = lane < L && (xs[lane] < 0 || xs[lane] >= P.V);   // L <= D <= 31
-  if (__any(bad)) {
-    for (int i = lane; i <= D; i += 64) toks[i] = -1;
-    if (lane == 0) {
-      P.out_len[b] = 0;
-      st_dev(&P.cur.pub[b].a, (unsigned long long)kNoDraw);
-    }
-    return;
-  }
-  if (greedy) {
-    for (int i = lane; i <= D; i += 64)
-      toks[i] = (i <= j) ? ld_dev(&P.pinfo[size_t(b) * (D + 1) + i].g) : -1;
-    if (lane == 0) {
-      P.out_len[b] = j + 1;
-      st_dev(&P.cur.pub[b].a, (unsigned long long)kNoDraw);
-    }
-    return;
-  }
-  for (int i = lane; i <= D; i += 64) {
-    if (i < j) toks[i] = xs[i];
-    else if (i > j) toks[i] = -1;      // position j is written by the final draw
-  }
-  // publish the final draw's descriptor (two self-validating words)
-  if (lane == 0) {
-    P.out_len[b] = j + 1;
-    const PosInfo* pi = P.pinfo + size_t(b) * (D + 1) + j;
-    const bool res = j < L;
-    const unsigned mt = __float_as_uint(ld_dev(&pi->mt));
-    const unsigned md = res ? __float_as_uint(ld_dev(&pi->md)) : 0u;
-    const unsigned lr = (res ? __float_as_uint(ld_dev(&pi->lnrho)) : 0u) | 1u;
-    st_dev(&P.cur.pub[b].c, ((unsigned long long)lr << 32) | md);
-    st_dev(&P.cur.pub[b].a, ((unsigned long long)mt << 32) |
-                                (unsigned long long)((res ? kResidual : kBonus) | (j << 2)));
-  }
-}
-
-// Evaluation of position p of sequence b once all its chunks are in (one wavefront).
-template <typename E>
-__device__ __forceinline__ void evaluate(const Params& P, int b, int p, int L, float T, bool greedy, int lane) {
-  const int D = P.D, R = P.R, nc = P.nchunk;
-  const RowPart* tpart = P.rpart + (size_t(b) * R + p) * nc;
-  const RowPart* dpart = P.rpart + (size_t(b) * R + D + 1 + p) * nc;
-  PosInfo* pi = P.pinfo + size_t(b) * (D + 1) + p;
-  bool reject = false;
-  if (greedy) {
-    float v = -INFINITY;
-    int idx = -1;
-    for (int c = lane; c < nc; c += 64)
-      am_combine(v, idx, ld_dev(&tpart[c].m), __float_as_int(ld_dev(&tpart[c].s)));
-    wave_am(v, idx);
-    if (p < L) reject = (P.tokens[size_t(b) * D + p] != idx);
-    if (lane == 0) {
-      st_dev(&pi->g, idx);
-      if (P.dbg_argmax) P.dbg_argmax[size_t(b) * (D + 1) + p] = idx;
-    }
-  } else {
-    const float k2 = kLog2e / T;
-    float mt = -INFINITY, stt = 0.f, md = -INFINITY, sd = 0.f;
-    for (int c = lane; c < nc; c += 64) {
-      ms_combine(mt, stt, ld_dev(&tpart[c].m), ld_dev(&tpart[c].s), k2);
-      if (p < L) ms_combine(md, sd, ld_dev(&dpart[c].m), ld_dev(&dpart[c].s), k2);
-    }
-    wave_ms(mt, stt, k2);
-    if (p < L) wave_ms(md, sd, k2);
-    const float lnt = logf(stt), lnd = logf(sd);
-    float lp = NAN, lq = NAN;
-    if (p < L) {
-      const int x = P.tokens[size_t(b) * D + p];
-      if (x >= 0 && x < P.V) {
-        const int cx = x / P.rch;
-        const float xt = ld_dev(&tpart[cx].xv);
-        const float xd = ld_dev(&dpart[cx].xv);
-        lp = (xt - mt) / T - lnt;
-        lq = (xd - md) / T - lnd;
-        const float ratio = expf(lp - lq);
-        reject = !(P.uniforms[size_t(b) * (D + 1) + p] < fminf(1.f, ratio));
-      } else {
-        reject = true;                 // invalid token: the decision marks the row
-      }
-    }
-    if (lane == 0) {
-      st_dev(&pi->mt, mt);
-      st_dev(&pi->md, md);
-      st_dev(&pi->lnrho, lnt - lnd);
-      if (P.dbg_row_stats) {
-        P.dbg_row_stats[(size_t(b) * R + p) * 2] = mt / T;
-        P.dbg_row_stats[(size_t(b) * R + p) * 2 + 1] = lnt;
-        if (p < L) {
-          P.dbg_row_stats[(size_t(b) * R + D + 1 + p) * 2] = md / T;
-          P.dbg_row_stats[(size_t(b) * R + D + 1 + p) * 2 + 1] = lnd;
-        }
-      }
-      if (P.dbg_logpq && p < L) {
-        P.dbg_logpq[(size_t(b) * D + p) * 2] = lp;
-        P.dbg_logpq[(size_t(b) * D + p) * 2 + 1] = lq;
-      }
-    }
-  }
-  unsigned long long old = 0;
-  if (lane == 0) {
-    wait_stores();
-    const unsigned long long bits = (1ull << p) | (reject ? (1ull << (32 + p)) : 0ull);
-    old = or_dev(P.cur.st + b, bits);
-    const unsigned long long now = old | bits;
-    int j0 = 0, j1 = 0;
-    const bool was = decided(old, L, j0);
-    const bool is = decided(now, L, j1);
-    old = (is && !was) ? (unsigned long long)(j1 + 1) : 0ull;
-  }
-  old = __shfl(old, 0);
-  if (old) decide<E>(P, b, L, T, greedy, int(old) - 1, lane);
-}
-
-// ------------------------------------------------------------------------------------------
-// row chunk: statistics of one 32 KB chunk (whole workgroup), then the pair counter and the
-// evaluation (wavefront 0 only; the other wavefronts return after the combine)
-
-template <typename E>
-__device__ __forceinline__ void row_chunk(const Params& P, Shared& sm, int b, int p, int which, int c, int L,
-                          float T, bool greedy, int tid) {
+__device__ __forceinline__ void row_chunk(const Params& P, Shared& sm, int b, int p, int which,
+                                          int c, int L, float T, bool greedy, int tid) {
   constexpr int kV = Elem<E>::kVec;
   const int D = P.D, nc = P.nchunk;
   const int r = which == 0 ? p : D + 1 + p;
@@ -584,19 +416,164 @@ __device__ __forceinline__ void row_chunk(const Params& P, Shared& sm, int b, in
     s = sum;
   }
 
-  // wavefront 0: publish the partial, count the pair's chunks, evaluate after the last one
-  const int lane = tid;
-  int last = 0;
-  if (lane == 0) {
+  if (tid == 0) {
     RowPart* out = P.rpart + (size_t(b) * P.R + r) * nc + c;
-    st_dev(&out->m, m);
-    st_dev(&out->s, s);
-    st_dev(&out->xv, xv);
-    wait_stores();
-    const unsigned done = add_dev(P.cur.pc + size_t(b) * (D + 1) + p, 1u) + 1u;
-    last = (done == unsigned(pair_chunks(p, L, greedy, nc))) ? 1 : 0;
+    *out = RowPart{m, s, xv, 0.f};
   }
-  if (uniform(__shfl(last, 0))) evaluate<E>(P, b, p, L, T, greedy, lane);
+}
+
+// ------------------------------------------------------------------------------------------
+// outcome of a sequence, from its row partials (one wavefront)
+
+struct Outcome {
+  unsigned mode;      // kNoDraw (greedy or invalid row), kResidual or kBonus
+  int j;              // position of the final token
+  float mt, md;       // exact maxima of target row j and (residual) draft row j
+  float lnrho;        // residual: fp32 ln(S_t / S_d) of row j, lowest bit forced to 1
+};
+
+struct RowScratch {   // combined statistics of a sequence's rows (one wavefront's)
+  float m[64], s[64], x[64];
+};
+
+__device__ inline int pow2_at_least(int n) {
+  int g = 1;
+  while (g < n) g <<= 1;
+  return g;
+}
+
+// Every wavefront that computes the outcome of sequence b from the same partials gets the same
+// bits (fixed combine trees, no data-dependent order). With `write`, the wavefront also stores
+// AL, the tokens other than the final draw's, the outcome words and the debug exports.
+template <typename E>
+__device__ __forceinline__ Outcome seq_outcome(const Params& P, int b, RowScratch& rs, int lane,
+                                               bool write) {
+  const int D = P.D, R = P.R, nc = P.nchunk;
+  const int L = P.lens ? P.lens[b] : D;
+  const float T = P.temperature[b];
+  const int32_t* xs = P.tokens + size_t(b) * D;
+  int32_t* toks = P.out_tokens + size_t(b) * (D + 1);
+  Outcome o = {kNoDraw, 0, 0.f, 0.f, 0.f};
+  bool valid = seq_valid(L, D, T);
+  if (valid) valid = !__any(lane < L && (xs[lane] < 0 || xs[lane] >= P.V));   // L <= D <= 31
+  if (!valid) {                        // the row is marked: AL 0, tokens -1
+    if (write) {
+      for (int i = lane; i <= D; i += 64) toks[i] = -1;
+      if (lane == 0) {
+        P.out_len[b] = 0;
+        P.pub[b] = SeqPub{(unsigned long long)kNoDraw, 0ull};
+      }
+    }
+    return o;
+  }
+  const bool greedy = (T == 0.f);
+  const float k2 = kLog2e / T;
+
+  // rows' statistics: G lanes per row (G a power of two), each lane combining chunks
+  // sub, sub + G, ...; then a butterfly inside the group
+  const int G = nc >= 64 ? 64 : pow2_at_least(nc);
+  const int RP = 64 / G;
+  const int sub = lane & (G - 1);
+  for (int r0 = 0; r0 < R; r0 += RP) {
+    const int r = r0 + lane / G;
+    const int p = r <= D ? r : r - (D + 1);
+    const bool need = r < R && (r <= D ? p <= L : (!greedy && p < L));
+    float m = -INFINITY, s = 0.f, x = 0.f;
+    int idx = -1;
+    if (need) {
+      const RowPart* rp = P.rpart + (size_t(b) * R + r) * nc;
+      for (int c = sub; c < nc; c += G) {
+        const RowPart q = rp[c];
+        if (greedy) {
+          am_combine(m, idx, q.m, __float_as_int(q.s));
+        } else {
+          ms_combine(m, s, q.m, q.s, k2);
+          x += q.xv;                   // zero except in the chunk holding the draft token
+        }
+      }
+    }
+    for (int off = G >> 1; off > 0; off >>= 1) {
+      const float m2 = __shfl_xor(m, off);
+      if (greedy) {
+        const int i2 = __shfl_xor(idx, off);
+        am_combine(m, idx, m2, i2);
+      } else {
+        const float s2 = __shfl_xor(s, off);
+        const float x2 = __shfl_xor(x, off);
+        ms_combine(m, s, m2, s2, k2);
+        x += x2;
+      }
+    }
+    if (sub == 0 && r < R) {
+      rs.m[r] = m;
+      rs.s[r] = greedy ? __int_as_float(idx) : s;
+      rs.x[r] = x;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // position p = lane: its test
+  const int p = lane;
+  bool rej = false;
+  int g = -1;
+  float mt = 0.f, md = 0.f, lr = 0.f;
+  if (p <= L) {
+    if (greedy) {
+      g = __float_as_int(rs.s[p]);
+      if (p < L) rej = xs[p] != g;
+      if (write && P.dbg_argmax) P.dbg_argmax[size_t(b) * (D + 1) + p] = g;
+    } else {
+      mt = rs.m[p];
+      const float lnt = logf(rs.s[p]);
+      float lnd = 0.f;
+      if (p < L) {
+        md = rs.m[D + 1 + p];
+        lnd = logf(rs.s[D + 1 + p]);
+        const float lp = (rs.x[p] - mt) / T - lnt;
+        const float lq = (rs.x[D + 1 + p] - md) / T - lnd;
+        const float ratio = expf(lp - lq);
+        rej = !(P.uniforms[size_t(b) * (D + 1) + p] < fminf(1.f, ratio));
+        lr = __uint_as_float(__float_as_uint(lnt - lnd) | 1u);
+        if (write && P.dbg_logpq) {
+          P.dbg_logpq[(size_t(b) * D + p) * 2] = lp;
+          P.dbg_logpq[(size_t(b) * D + p) * 2 + 1] = lq;
+        }
+        if (write && P.dbg_row_stats) {
+          P.dbg_row_stats[(size_t(b) * R + D + 1 + p) * 2] = md / T;
+          P.dbg_row_stats[(size_t(b) * R + D + 1 + p) * 2 + 1] = lnd;
+        }
+      }
+      if (write && P.dbg_row_stats) {
+        P.dbg_row_stats[(size_t(b) * R + p) * 2] = mt / T;
+        P.dbg_row_stats[(size_t(b) * R + p) * 2 + 1] = lnt;
+      }
+    }
+  }
+  const unsigned long long rejm = __ballot(rej);
+  const int j = rejm ? int(__builtin_ctzll(rejm)) : L;
+  o.j = j;
+  o.mode = greedy ? kNoDraw : (j < L ? kResidual : kBonus);
+  o.mt = __shfl(mt, j);
+  o.md = __shfl(md, j);
+  o.lnrho = __shfl(lr, j);
+  if (write) {
+    if (lane <= D) {
+      if (greedy) toks[lane] = lane <= j ? g : -1;
+      else if (lane < j) toks[lane] = xs[lane];
+      else if (lane > j) toks[lane] = -1;      // position j is written by the final draw
+    }
+    if (lane == 0) {
+      P.out_len[b] = j + 1;
+      const unsigned long long a = greedy ? (unsigned long long)kNoDraw
+          : ((unsigned long long)__float_as_uint(o.mt) << 32) | (o.mode | (unsigned(j) << 2));
+      const unsigned long long c = greedy ? 0ull
+          : ((unsigned long long)(__float_as_uint(o.lnrho) | 1u) << 32) | __float_as_uint(o.md);
+      P.pub[b] = SeqPub{a, c};
+    }
+  }
+  return o;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -645,18 +622,17 @@ struct Draw {           // what the fp64 evaluation of one sequence's final row(
   double lnrho, u;
 };
 
-// The draw of sequence b from its published words (wave-uniform arguments); e2 in shared memory.
-__device__ inline Draw make_draw(const Params& P, int b, unsigned long long a,
-                                 unsigned long long c, const double* e2) {
+// The draw of sequence b from its outcome (wave-uniform); e2 in shared memory.
+__device__ inline Draw make_draw(const Params& P, int b, const Outcome& o, const double* e2) {
   constexpr double k256 = 369.3299304675746;          // 256 / ln 2
   Draw w;
-  w.residual = unsigned(a & 3u) == kResidual;
-  w.j = int((a >> 2) & 31u);
+  w.residual = o.mode == kResidual;
+  w.j = o.j;
   const double T = double(P.temperature[b]);
   w.u = double(P.uniforms[size_t(b) * (P.D + 1) + P.D]);
-  w.lnrho = double(__uint_as_float(unsigned(c >> 32)));
-  const double mt = double(__uint_as_float(unsigned(a >> 32)));
-  const double md = double(__uint_as_float(unsigned(c)));
+  w.lnrho = double(o.lnrho);
+  const double mt = double(o.mt);
+  const double md = double(o.md);
   const double c1 = k256 / T;
   w.t = RowExp{c1, -mt * c1, e2};
   w.d = RowExp{c1, -md * c1, e2};
@@ -730,18 +706,18 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
   const bool one = nF <= 64;
   FinPart r = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, INFINITY, -INFINITY};
   if (one && lane < nF) {
-    const double* q = reinterpret_cast<const double*>(fp + lane);
-    r.st = ld_dev(q + 0); r.sd = ld_dev(q + 1); r.at = ld_dev(q + 2); r.ad = ld_dev(q + 3);
-    r.bt = ld_dev(q + 4); r.bd = ld_dev(q + 5); r.dmin = ld_dev(q + 6); r.dmax = ld_dev(q + 7);
+    const FinPart& q = fp[lane];
+    r.st = q.st; r.sd = q.sd; r.at = q.at; r.ad = q.ad;
+    r.bt = q.bt; r.bd = q.bd; r.dmin = q.dmin; r.dmax = q.dmax;
   }
   // the record of item f (f = lane + 64 k, this lane's)
   auto rec = [&](int f) {
     if (one) return r;
     FinPart x = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, INFINITY, -INFINITY};
     if (f < nF) {
-      const double* q = reinterpret_cast<const double*>(fp + f);
-      x.st = ld_dev(q + 0); x.sd = ld_dev(q + 1); x.at = ld_dev(q + 2); x.ad = ld_dev(q + 3);
-      x.bt = ld_dev(q + 4); x.bd = ld_dev(q + 5); x.dmin = ld_dev(q + 6); x.dmax = ld_dev(q + 7);
+      const FinPart& q = fp[f];
+      x.st = q.st; x.sd = q.sd; x.at = q.at; x.ad = q.ad;
+      x.bt = q.bt; x.bd = q.bd; x.dmin = q.dmin; x.dmax = q.dmax;
     }
     return x;
   };
@@ -826,13 +802,13 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
   const FinPart* rf = fp + fstar;
   const bool bonus = !w.residual;
   const bool blockwise = !past_end && !slow && (bonus || (!target_only &&
-                         !(ld_dev(&rf->dmin) <= ld_dev(&rf->dmax))));
+                         !(rf->dmin <= rf->dmax)));
   int kfirst = 0, klast = KB - 1;
   if (blockwise) {
     double bm = 0.0;                   // lane k: mass of block k
     if (lane < KB) {
-      const double ka = ld_dev(&rf->kat[lane]);
-      bm = bonus ? ka : fmax(0.0, ka * it - ld_dev(&rf->kad[lane]) * id);
+      const double ka = rf->kat[lane];
+      bm = bonus ? ka : fmax(0.0, ka * it - rf->kad[lane] * id);
     }
     const double inc = dpp_scan_add(bm) + run;
     const unsigned long long over = __ballot(lane < KB && inc > t);
@@ -1008,7 +984,7 @@ __device__ inline unsigned long long uniform64(unsigned long long v) {
   return ((unsigned long long)hi << 32) | lo;
 }
 
-// Does a sequence's published pair (a, c) call for a final draw that items can start on?
+// Does a sequence's outcome pair (a, c) call for a final draw?
 __device__ inline bool draw_ready(unsigned long long a, unsigned long long c) {
   return unsigned(a & 3u) >= kResidual && ((c >> 32) & 1u);
 }
@@ -1028,35 +1004,23 @@ __device__ __forceinline__ void row_workgroup(const Params& P, Shared& sm, int r
   const int D = P.D;
   const int L = P.lens ? P.lens[b] : D;
   const float T = P.temperature[b];
-  if (!seq_valid(L, D, T)) {
-    // invalid length or temperature: one wavefront of the sequence marks the row
-    if (p == 0 && which == 0 && c == 0 && tid < 64) {
-      int32_t* toks = P.out_tokens + size_t(b) * (D + 1);
-      for (int i = tid; i <= D; i += 64) toks[i] = -1;
-      if (tid == 0) {
-        P.out_len[b] = 0;
-        st_dev(&P.cur.pub[b].a, (unsigned long long)kNoDraw);
-      }
-    }
-    return;
-  }
+  if (!seq_valid(L, D, T)) return;    // invalid length or temperature: nothing is read
   const bool greedy = (T == 0.f);
   if (which == 0 ? (p <= L) : (!greedy && p < L))      // rows the method needs
     row_chunk<E>(P, sm, b, p, which, c, L, T, greedy, tid);
 }
 
-// Final-draw item wavefront: item g = b * nF + f, after the row kernel (every sequence is
-// decided).
+// Final-draw item wavefront: item g = b * nF + f (wave-uniform), after the row kernel. Item 0
+// of each sequence writes the sequence's outcome.
 template <typename E>
-__device__ __forceinline__ void item_wavefront(const Params& P, const double* e2, int g,
-                                               int lane) {
+__device__ __forceinline__ void item_wavefront(const Params& P, const double* e2, RowScratch& rs,
+                                               int g, int lane) {
   if (g >= P.B * P.nF) return;
   const int b = g / P.nF;
   const int f = g - b * P.nF;
-  const unsigned long long a = uniform64(ld_dev(&P.cur.pub[b].a));
-  const unsigned long long c = uniform64(ld_dev(&P.cur.pub[b].c));
-  if (!draw_ready(a, c)) return;       // no draw for this sequence (greedy or invalid)
-  const Draw w = make_draw(P, b, a, c, e2);
+  const Outcome o = seq_outcome<E>(P, b, rs, lane, f == 0);
+  if (o.mode != kResidual && o.mode != kBonus) return;   // no draw (greedy or invalid)
+  const Draw w = make_draw(P, b, o, e2);
   ItemRuns<E> tr, dr;
   tr.load(final_row<E>(P, b, w.j, false), f * kItemElems<E>, P.V, lane);
   if (w.residual) dr.load(final_row<E>(P, b, w.j, true), f * kItemElems<E>, P.V, lane);
@@ -1067,23 +1031,12 @@ __device__ __forceinline__ void item_wavefront(const Params& P, const double* e2
 template <typename E>
 __device__ __forceinline__ void pick_wavefront(const Params& P, const double* e2, int b, int lane) {
   if (b >= P.B) return;
-  const unsigned long long a = uniform64(ld_dev(&P.cur.pub[b].a));
-  const unsigned long long c = uniform64(ld_dev(&P.cur.pub[b].c));
+  const unsigned long long a = uniform64(P.pub[b].a);
+  const unsigned long long c = uniform64(P.pub[b].c);
   if (!draw_ready(a, c)) return;
-  wave_pick<E>(P, b, make_draw(P, b, a, c, e2), lane);
-}
-
-// Clears the next call's counters (spread over the pick workgroups).
-__device__ inline void clear_next(const Params& P, int wid, int tid) {
-  const long long stride = (long long)P.n_pick * kThreads;
-  const long long me = (long long)wid * kThreads + tid;
-  for (long long i = me; i < P.B; i += stride) {
-    P.nxt.st[i] = 0ull;
-    P.nxt.pub[i].a = 0ull;
-    P.nxt.pub[i].c = 0ull;
-  }
-  const long long npc = (long long)P.B * (P.D + 1);
-  for (long long i = me; i < npc; i += stride) P.nxt.pc[i] = 0u;
+  const Outcome o = {unsigned(a & 3u), int((a >> 2) & 31u), __uint_as_float(unsigned(a >> 32)),
+                     __uint_as_float(unsigned(c)), __uint_as_float(unsigned(c >> 32))};
+  wave_pick<E>(P, b, make_draw(P, b, o, e2), lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1096,15 +1049,17 @@ __global__ __launch_bounds__(kThreads) void row_kernel(Params P) {
   row_workgroup<E>(P, sm, int(blockIdx.x), threadIdx.x);
 }
 
-// Final-draw kernels, after the row kernel: partial sums (one wavefront per item), then the
-// pick (one wavefront per sequence), which also clears the next call's counters.
+// Final-draw kernels, after the row kernel: outcome and partial sums (one wavefront per item),
+// then the pick (one wavefront per sequence).
 template <typename E>
 __global__ __launch_bounds__(kThreads) void item_kernel(Params P) {
   __shared__ double e2[256];
+  __shared__ RowScratch rs[kWaves];
   const int tid = threadIdx.x;
   for (int i = tid; i < 256; i += kThreads) e2[i] = exp2(double(i) / 256.0);
   __syncthreads();
-  item_wavefront<E>(P, e2, int(blockIdx.x) * kWaves + (tid >> 6), tid & 63);
+  const int wave = uniform(tid >> 6);
+  item_wavefront<E>(P, e2, rs[wave], int(blockIdx.x) * kWaves + wave, tid & 63);
 }
 
 template <typename E>
@@ -1113,14 +1068,7 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(Params P) {
   const int tid = threadIdx.x;
   for (int i = tid; i < 256; i += kThreads) e2[i] = exp2(double(i) / 256.0);
   __syncthreads();
-  pick_wavefront<E>(P, e2, int(blockIdx.x) * kWaves + (tid >> 6), tid & 63);
-  clear_next(P, int(blockIdx.x), tid);
-}
-
-// Clears the counter region (when a workspace meets a new layout).
-__global__ void clear_kernel(unsigned* p, long long n) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+  pick_wavefront<E>(P, e2, int(blockIdx.x) * kWaves + uniform(tid >> 6), tid & 63);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1133,14 +1081,12 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // sequence) outnumber the items of the whole batch.
 inline int item_elems(int elem_bytes) { return kRowChunkBytes / elem_bytes / kItemsPerChunk; }
 
-// Workspace: [counter set 0][counter set 1] [row partials][position info]
-//            [final-draw partials][pick scratch]. A counter set is [st B][pc B(D+1)][pub B];
-//            both sets must be zero when a workspace is first used. One layout serves both
-//            dtypes (nF and nchunk are those of the dtype with more).
+// Workspace: [outcome words B][row partials][final-draw partials][pick scratch]. Every part is
+// written before it is read within one call, so a workspace needs no initialisation. One
+// layout serves both dtypes (nF and nchunk are those of the dtype with more).
 struct Layout {
   int nchunk, nF;
-  size_t set_bytes, off_st, off_pc, off_pub;   // within a counter set
-  size_t off_rpart, off_pinfo, off_fpart, off_fmass, total;
+  size_t off_pub, off_rpart, off_fpart, off_fmass, total;
 };
 
 inline bool make_layout(int B, int D, int V, Layout& L) {
@@ -1148,15 +1094,10 @@ inline bool make_layout(int B, int D, int V, Layout& L) {
   const int rch = kRowChunkBytes / 4, fch = item_elems(4);      // fp32: the most chunks/items
   L.nchunk = int((size_t(V) + rch - 1) / rch);
   L.nF = int((size_t(V) + fch - 1) / fch);
-  size_t o = 0;
-  L.off_st = o;    o += align256(size_t(B) * 8);
-  L.off_pc = o;    o += align256(size_t(B) * (D + 1) * 4);
-  L.off_pub = o;   o += align256(size_t(B) * sizeof(SeqPub));
-  L.set_bytes = o;
-  o = 2 * L.set_bytes;
   const size_t R = size_t(2) * D + 1;
+  size_t o = 0;
+  L.off_pub = o;   o += align256(size_t(B) * sizeof(SeqPub));
   L.off_rpart = o; o += align256(size_t(B) * R * L.nchunk * sizeof(RowPart));
-  L.off_pinfo = o; o += align256(size_t(B) * (D + 1) * sizeof(PosInfo));
   L.off_fpart = o; o += align256(size_t(B) * L.nF * sizeof(FinPart));
   L.off_fmass = o; o += align256(size_t(B) * L.nF * sizeof(double));
   L.total = o;
@@ -1168,28 +1109,13 @@ inline size_t workspace_bytes(int B, int D, int V) {
   return make_layout(B, D, V, a) ? a.total : 0;
 }
 
-inline CounterSet counter_set(char* base, const Layout& L, int k) {
-  char* s = base + size_t(k) * L.set_bytes;
-  CounterSet c;
-  c.st = reinterpret_cast<unsigned long long*>(s + L.off_st);
-  c.pc = reinterpret_cast<unsigned*>(s + L.off_pc);
-  c.pub = reinterpret_cast<SeqPub*>(s + L.off_pub);
-  return c;
-}
-
 struct DeviceWorkspace {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
 
-struct WsState {      // host-side knowledge about one workspace
-  long long calls = 0;        // calls made with it (the parity picks the counter set)
-  int B = -1, D = -1, V = -1; // layout of the last call (-1: zero-filled, unused)
-};
-
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, DeviceWorkspace> g_ws;   // library buffers per stream
-std::map<void*, WsState> g_ws_state;
 
 struct Profile {        // optional timing of the kernel: one event pair per call
   std::vector<hipEvent_t> begin, end;
@@ -1215,7 +1141,6 @@ int launch(Params& P, hipStream_t stream) {
   const long long items = ((long long)P.B * P.nF + kWaves - 1) / kWaves;
   const long long picks = ((long long)P.B + kWaves - 1) / kWaves;
   if (rows > 0x7fffffffll || items > 0x7fffffffll) return SV_EINVAL;
-  P.n_pick = int(picks);
 
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   {
@@ -1263,30 +1188,15 @@ int run(int dtype, const void* target, const void* draft, const int32_t* tokens,
         // earlier calls on this stream may still use the old buffer
         if (hipStreamSynchronize(stream) != hipSuccess) return SV_EHIP;
         (void)hipFree(w.ptr);
-        g_ws_state.erase(w.ptr);
         w.ptr = nullptr;
         w.bytes = 0;
       }
       if (hipMalloc(&w.ptr, need) != hipSuccess) { w.ptr = nullptr; return SV_ENOMEM; }
-      if (hipMemset(w.ptr, 0, need) != hipSuccess) return SV_EHIP;   // counters start at zero
       w.bytes = need;
     }
     ws = w.ptr;
   }
-  WsState& state = g_ws_state[ws];
   char* base = static_cast<char*>(ws);
-  if (state.B >= 0 && (state.B != B || state.D != D || state.V != V)) {
-    // the layout changed: clear both counter sets (a small kernel, graph-safe)
-    const long long n = (long long)(2 * lay.set_bytes / 4);
-    hipLaunchKernelGGL(clear_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream,
-                       reinterpret_cast<unsigned*>(base), n);
-    if (hipGetLastError() != hipSuccess) return SV_EHIP;
-  }
-  state.B = B;
-  state.D = D;
-  state.V = V;
-  const int parity = int(state.calls & 1);
-  ++state.calls;
 
   Params P = {};
   P.target = target;
@@ -1305,10 +1215,8 @@ int run(int dtype, const void* target, const void* draft, const int32_t* tokens,
   P.nchunk = int((size_t(V) + P.rch - 1) / P.rch);
   P.fch = item_elems(elem_bytes);
   P.nF = int((size_t(V) + P.fch - 1) / P.fch);
-  P.cur = counter_set(base, lay, parity);
-  P.nxt = counter_set(base, lay, 1 - parity);
+  P.pub = reinterpret_cast<SeqPub*>(base + lay.off_pub);
   P.rpart = reinterpret_cast<RowPart*>(base + lay.off_rpart);
-  P.pinfo = reinterpret_cast<PosInfo*>(base + lay.off_pinfo);
   P.fpart = reinterpret_cast<FinPart*>(base + lay.off_fpart);
   P.fmass = reinterpret_cast<double*>(base + lay.off_fmass);
   P.dbg_row_stats = dbg_stats;

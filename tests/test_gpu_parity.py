@@ -156,7 +156,10 @@ def test_invalid_rows_marked_on_gpu():
 def test_caller_workspace_matches_library_workspace():
     import sampling_spec_verify_02_amd as sv
     w = make("c5", 11, B=96)
-    ws = torch.zeros(sv.workspace_bytes(w.B, w.D, w.V), dtype=torch.uint8, device="cuda:0")
+    # a workspace needs no initialisation: start from arbitrary bytes
+    g = torch.Generator().manual_seed(5)
+    n = sv.workspace_bytes(w.B, w.D, w.V)
+    ws = torch.randint(0, 256, (n,), dtype=torch.uint8, generator=g).to("cuda:0")
     a = G.run(w)
     b = G.run(w, workspace=ws)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
@@ -195,8 +198,8 @@ def test_lossless_chi_square_on_gpu():
 
 
 def test_workspace_reuse_across_batch_sizes():
-    """The per-sequence counters live at fixed offsets: a workspace used for a small batch and
-    then a larger one must still give exact results (the library clears the new slots)."""
+    """One workspace serves calls of different batch sizes in turn: nothing a call leaves in it
+    may leak into the next call's results."""
     import sampling_spec_verify_02_amd as sv
     ws = torch.zeros(sv.workspace_bytes(300, 7, 129280), dtype=torch.uint8, device="cuda:0")
     for B, seed in ((40, 1), (300, 2), (17, 3), (300, 4)):
