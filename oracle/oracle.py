@@ -190,7 +190,9 @@ def verify(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray,
             res.row_max_t[b, i], res.row_logsum_t[b, i] = mt, lst
             res.row_max_d[b, i], res.row_logsum_d[b, i] = md, lsd
             res.logp_x[b, i], res.logq_x[b, i] = lp[x[i]], lq[x[i]]
-            ratio = math.exp(lp[x[i]] - lq[x[i]])
+            # p/q = exp(log p - log q); beyond the double range it is +inf (an acceptance)
+            d = lp[x[i]] - lq[x[i]]
+            ratio = math.exp(d) if d < 709.0 else math.inf
             u = float(uniforms[b, i])
             if abs(u - ratio) < FLAG_TOL:
                 res.flagged[b] = True

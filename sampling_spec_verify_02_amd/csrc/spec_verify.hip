@@ -129,6 +129,18 @@ __device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "me
 // element access
 
 template <typename E> struct Elem;
+// Running maximum of packed values. bf16 pairs are compared as fp16 pairs (one packed max per
+// word): both formats are sign-magnitude with the magnitude ordered like its bit pattern, so
+// the fp16 order of the halves is the bf16 order of the values they hold, for every bf16 value
+// below 2^121 in magnitude. The larger ones fall on fp16's inf / NaN patterns, which the packed
+// max passes over (quiet NaN), returns (inf) or turns into the canonical NaN (signalling NaN);
+// the row chunk detects each outcome and redoes its max exactly.
+__device__ inline uint32_t pk_max_bf16(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_max_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 template <> struct Elem<uint16_t> {          // bf16 bit patterns
   static constexpr int kVec = 8;             // elements per 16-byte load
   __device__ static float get(const uint16_t* p, size_t i) {
@@ -138,6 +150,17 @@ template <> struct Elem<uint16_t> {          // bf16 bit patterns
     const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
     return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
   }
+  static constexpr uint32_t kNegInf = 0xff80ff80u;    // two bf16 -inf (fp16 quiet NaNs: a
+                                                       // packed max passes them over)
+  // packed running max (see pk_max_bf16); identity: the packed pattern of two -inf (fp16)
+  typedef uint32_t Acc;
+  __device__ static Acc acc_init() { return 0xfc00fc00u; }
+  __device__ static Acc acc_add(Acc a, const uint4& v) {
+    return pk_max_bf16(pk_max_bf16(a, v.x), pk_max_bf16(pk_max_bf16(v.y, v.z), v.w));
+  }
+  __device__ static float acc_value(Acc a) {
+    return fmaxf(__uint_as_float(a << 16), __uint_as_float(a & 0xffff0000u));
+  }
 };
 template <> struct Elem<float> {
   static constexpr int kVec = 4;
@@ -145,6 +168,14 @@ template <> struct Elem<float> {
   __device__ static float lane(const uint4& v, int e) {
     return __uint_as_float(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
   }
+  static constexpr uint32_t kNegInf = 0xff800000u;
+  typedef float Acc;
+  __device__ static Acc acc_init() { return -INFINITY; }
+  __device__ static Acc acc_add(Acc a, const uint4& v) {
+    return fmaxf(fmaxf(a, __uint_as_float(v.x)),
+                 fmaxf(fmaxf(__uint_as_float(v.y), __uint_as_float(v.z)), __uint_as_float(v.w)));
+  }
+  __device__ static float acc_value(Acc a) { return a; }
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -172,6 +203,11 @@ template <> struct Run<uint16_t> {
         w[k] = lo | (hi << 16);
       }
     }
+  }
+  // the full run at q, 16-byte aligned
+  __device__ __forceinline__ void load_vec(const uint16_t* q) {
+    const uint4 v = *reinterpret_cast<const uint4*>(q);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   }
   __device__ float at(int e) const {
     return __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
@@ -201,6 +237,12 @@ template <> struct Run<float> {
 #pragma unroll
       for (int e = 0; e < kFinPer; ++e) x[e] = (e < n) ? q[e] : 0.f;
     }
+  }
+  __device__ __forceinline__ void load_vec(const float* q) {
+    const float4 v0 = reinterpret_cast<const float4*>(q)[0];
+    const float4 v1 = reinterpret_cast<const float4*>(q)[1];
+    x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+    x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
   }
   __device__ float at(int e) const { return x[e]; }
   __device__ Run opaque() const {
@@ -258,6 +300,16 @@ __device__ inline void wave_am(float& v, int& i) {
     const int i2 = __shfl_xor(i, off);
     am_combine(v, i, v2, i2);
   }
+}
+
+// ms_combine without branches, for operands that are either empty (m = -inf, s = 0) or
+// non-empty (s > 0); the same result for (a, b) as for (b, a).
+__device__ inline void ms_merge(float& m, float& s, float m2, float s2, float k) {
+  const float mn = fmaxf(m, m2);
+  const float a = s == 0.f ? 0.f : s * __builtin_amdgcn_exp2f((m - mn) * k);
+  const float c = s2 == 0.f ? 0.f : s2 * __builtin_amdgcn_exp2f((m2 - mn) * k);
+  s = a + c;
+  m = mn;
 }
 
 // Inclusive scans of a double over the 64 lanes with DPP row shifts and row broadcasts (VALU
@@ -340,11 +392,25 @@ __device__ __forceinline__ void row_chunk(const Params& P, Shared& sm, int b, in
   const bool aligned = (reinterpret_cast<uintptr_t>(ptr) & 15) == 0;
   const int nvec = aligned ? n / kV : 0;
 
+  // the thread's vectors tid + 256 k; past nvec they hold -inf (no weight, never the max), and
+  // the load repeats the last vector so that every load is unconditional
+  const uint4* vp = reinterpret_cast<const uint4*>(ptr);
   uint4 buf[kRowVecs];
+  if (nvec == kRowVecs * kThreads) {
 #pragma unroll
-  for (int k = 0; k < kRowVecs; ++k) {
-    const int vi = tid + k * kThreads;
-    if (vi < nvec) buf[k] = load_stream(reinterpret_cast<const uint4*>(ptr) + vi);
+    for (int k = 0; k < kRowVecs; ++k) buf[k] = load_stream(vp + tid + k * kThreads);
+  } else {
+    const uint4 ninf = make_uint4(Elem<E>::kNegInf, Elem<E>::kNegInf, Elem<E>::kNegInf,
+                                  Elem<E>::kNegInf);
+#pragma unroll
+    for (int k = 0; k < kRowVecs; ++k) {
+      const int vi = tid + k * kThreads;
+      buf[k] = ninf;
+      if (nvec > 0) {
+        const uint4 v = load_stream(vp + min(vi, nvec - 1));
+        if (vi < nvec) buf[k] = v;
+      }
+    }
   }
   float xv = 0.f;
   if (!greedy && tid == 0 && p < L) {
@@ -377,26 +443,38 @@ __device__ __forceinline__ void row_chunk(const Params& P, Shared& sm, int b, in
     m = best;
     s = __int_as_float(bi < 0 ? -1 : c0 + bi);
   } else {
-    // online max / sum per 16-byte vector: only one vector's elements are live at a time
+    // the thread's max over its vectors (packed), then one pass of exp2 sums against it
     const float k2 = kLog2e / T;
-    float mx = -INFINITY, sum = 0.f;
+    typename Elem<E>::Acc acc = Elem<E>::acc_init();
 #pragma unroll
-    for (int k = 0; k < kRowVecs; ++k) {
-      const int vi = tid + k * kThreads;
-      if (vi < nvec) {
-        float mk = Elem<E>::lane(buf[k], 0);
+    for (int k = 0; k < kRowVecs; ++k) acc = Elem<E>::acc_add(acc, buf[k]);
+    float mx = tid < nvec ? Elem<E>::acc_value(acc) : -INFINITY;
+    float sum = 0.f;
+    if (tid < nvec) {
+      const float off = -mx * k2;
 #pragma unroll
-        for (int e = 1; e < kV; ++e) mk = fmaxf(mk, Elem<E>::lane(buf[k], e));
-        if (k == 0) {
-          mx = mk;
-        } else {
-          const float mn = fmaxf(mx, mk);
-          sum *= __builtin_amdgcn_exp2f((mx - mn) * k2);
-          mx = mn;
+      for (int k = 0; k < kRowVecs; ++k) {
+#pragma unroll
+        for (int e = 0; e < kV; ++e)
+          sum += __builtin_amdgcn_exp2f(fmaf(Elem<E>::lane(buf[k], e), k2, off));
+      }
+    }
+    // Exact redo where the packed max may not be the max: it landed on an fp16 inf / NaN
+    // pattern (|value| >= 2^121), or passed over such a value and the sum overflowed.
+    if (!(sum < INFINITY) || !(fabsf(mx) < 0x1p121f)) {
+      mx = -INFINITY;
+      sum = 0.f;
+      for (int k = 0; k < kRowVecs; ++k) {
+        if (tid + k * kThreads < nvec) {
+          for (int e = 0; e < kV; ++e) {
+            const float x = Elem<E>::lane(buf[k], e);
+            if (x > mx) {
+              sum = (sum == 0.f) ? 0.f : sum * __builtin_amdgcn_exp2f((mx - x) * k2);
+              mx = x;
+            }
+            sum += __builtin_amdgcn_exp2f((x - mx) * k2);
+          }
         }
-        const float off = -mx * k2;
-#pragma unroll
-        for (int e = 0; e < kV; ++e) sum += __builtin_amdgcn_exp2f(fmaf(Elem<E>::lane(buf[k], e), k2, off));
       }
     }
     for (int i = nvec * kV + tid; i < n; i += kThreads) {
@@ -430,32 +508,82 @@ struct Outcome {
   int j;              // position of the final token
   float mt, md;       // exact maxima of target row j and (residual) draft row j
   float lnrho;        // residual: fp32 ln(S_t / S_d) of row j, lowest bit forced to 1
+  float u;            // the final draw's uniform
 };
 
-struct RowScratch {   // combined statistics of a sequence's rows (one wavefront's)
-  float m[64], s[64], x[64];
+constexpr int kPartBatch = 8;   // chunk partials a lane loads at once
+
+// The statistics of row r (lane r) from chunk partials c0 .. c0 + 7 (those below nc), merged
+// into (m, s, x): max first, then one exp2 per chunk.
+__device__ inline void merge_batch(const RowPart (&q)[kPartBatch], int c0, int nc, float k2,
+                                   float& m, float& s, float& x) {
+  float mb = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kPartBatch; ++i)
+    if (c0 + i < nc) mb = fmaxf(mb, q[i].m);
+  float sb = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPartBatch; ++i)
+    if (c0 + i < nc && q[i].s != 0.f) sb = fmaf(q[i].s, __builtin_amdgcn_exp2f((q[i].m - mb) * k2), sb);
+#pragma unroll
+  for (int i = 0; i < kPartBatch; ++i)
+    if (c0 + i < nc) x += q[i].xv;     // zero except in the chunk holding the draft token
+  ms_merge(m, s, mb, sb, k2);
+}
+__device__ inline void argmax_batch(const RowPart (&q)[kPartBatch], int c0, int nc, float& v,
+                                    int& idx) {
+#pragma unroll
+  for (int i = 0; i < kPartBatch; ++i)
+    if (c0 + i < nc) am_combine(v, idx, q[i].m, __float_as_int(q[i].s));
+}
+
+// What the outcome of a sequence reads, loaded in one go: lane r < R the first batch of row r's
+// chunk partials (target rows 0..D, then draft rows 0..D-1; loaded whether the row is needed or
+// not, the workspace being always readable), lane p its draft token and uniform.
+struct OutcomeIn {
+  RowPart q[kPartBatch];
+  int L;
+  float T;
+  int xl;
+  float ul;
 };
 
-__device__ inline int pow2_at_least(int n) {
-  int g = 1;
-  while (g < n) g <<= 1;
-  return g;
+__device__ __forceinline__ OutcomeIn load_outcome(const Params& P, int b, int lane) {
+  const int D = P.D, R = P.R, nc = P.nchunk;
+  OutcomeIn in;
+  const RowPart* rp = P.rpart + (size_t(b) * R + lane) * nc;
+#pragma unroll
+  for (int i = 0; i < kPartBatch; ++i)
+    if (lane < R && i < nc) in.q[i] = rp[i];
+  in.L = P.lens ? P.lens[b] : D;
+  in.T = P.temperature[b];
+  in.xl = lane < D ? P.tokens[size_t(b) * D + lane] : 0;
+  in.ul = lane <= D ? P.uniforms[size_t(b) * (D + 1) + lane] : 0.f;
+  return in;
 }
 
 // Every wavefront that computes the outcome of sequence b from the same partials gets the same
-// bits (fixed combine trees, no data-dependent order). With `write`, the wavefront also stores
-// AL, the tokens other than the final draw's, the outcome words and the debug exports.
+// bits (fixed combine order). With `write`, the wavefront also stores AL, the tokens other than
+// the final draw's, the outcome words and the debug exports.
 template <typename E>
-__device__ __forceinline__ Outcome seq_outcome(const Params& P, int b, RowScratch& rs, int lane,
-                                               bool write) {
+__device__ __forceinline__ Outcome seq_outcome(const Params& P, int b, const OutcomeIn& in,
+                                               int lane, bool write) {
   const int D = P.D, R = P.R, nc = P.nchunk;
-  const int L = P.lens ? P.lens[b] : D;
-  const float T = P.temperature[b];
-  const int32_t* xs = P.tokens + size_t(b) * D;
+  // Lane r < R holds row r and combines its chunk partials in order.
+  const int r = lane;
+  const RowPart* rp = P.rpart + (size_t(b) * R + r) * nc;
+  RowPart q[kPartBatch];
+#pragma unroll
+  for (int i = 0; i < kPartBatch; ++i) q[i] = in.q[i];
+  const int L = in.L;
+  const float T = in.T;
+  const int xl = in.xl;
+  const float ul = in.ul;
   int32_t* toks = P.out_tokens + size_t(b) * (D + 1);
-  Outcome o = {kNoDraw, 0, 0.f, 0.f, 0.f};
+
+  Outcome o = {kNoDraw, 0, 0.f, 0.f, 0.f, 0.f};
   bool valid = seq_valid(L, D, T);
-  if (valid) valid = !__any(lane < L && (xs[lane] < 0 || xs[lane] >= P.V));   // L <= D <= 31
+  if (valid) valid = !__any(lane < L && (xl < 0 || xl >= P.V));    // L <= D <= 31
   if (!valid) {                        // the row is marked: AL 0, tokens -1
     if (write) {
       for (int i = lane; i <= D; i += 64) toks[i] = -1;
@@ -467,53 +595,26 @@ __device__ __forceinline__ Outcome seq_outcome(const Params& P, int b, RowScratc
     return o;
   }
   const bool greedy = (T == 0.f);
-  const float k2 = kLog2e / T;
-
-  // rows' statistics: G lanes per row (G a power of two), each lane combining chunks
-  // sub, sub + G, ...; then a butterfly inside the group
-  const int G = nc >= 64 ? 64 : pow2_at_least(nc);
-  const int RP = 64 / G;
-  const int sub = lane & (G - 1);
-  for (int r0 = 0; r0 < R; r0 += RP) {
-    const int r = r0 + lane / G;
-    const int p = r <= D ? r : r - (D + 1);
-    const bool need = r < R && (r <= D ? p <= L : (!greedy && p < L));
-    float m = -INFINITY, s = 0.f, x = 0.f;
-    int idx = -1;
-    if (need) {
-      const RowPart* rp = P.rpart + (size_t(b) * R + r) * nc;
-      for (int c = sub; c < nc; c += G) {
-        const RowPart q = rp[c];
-        if (greedy) {
-          am_combine(m, idx, q.m, __float_as_int(q.s));
-        } else {
-          ms_combine(m, s, q.m, q.s, k2);
-          x += q.xv;                   // zero except in the chunk holding the draft token
-        }
-      }
-    }
-    for (int off = G >> 1; off > 0; off >>= 1) {
-      const float m2 = __shfl_xor(m, off);
-      if (greedy) {
-        const int i2 = __shfl_xor(idx, off);
-        am_combine(m, idx, m2, i2);
-      } else {
-        const float s2 = __shfl_xor(s, off);
-        const float x2 = __shfl_xor(x, off);
-        ms_combine(m, s, m2, s2, k2);
-        x += x2;
-      }
-    }
-    if (sub == 0 && r < R) {
-      rs.m[r] = m;
-      rs.s[r] = greedy ? __int_as_float(idx) : s;
-      rs.x[r] = x;
+  const float iT = 1.f / T;
+  const float k2 = kLog2e * iT;
+  const int pr = r <= D ? r : r - (D + 1);
+  const bool need = r < R && (r <= D ? pr <= L : (!greedy && pr < L));
+  float m = -INFINITY, s = 0.f, x = 0.f;
+  int idx = -1;
+  if (need) {
+    if (greedy) argmax_batch(q, 0, nc, m, idx);
+    else merge_batch(q, 0, nc, k2, m, s, x);
+    for (int c0 = kPartBatch; c0 < nc; c0 += kPartBatch) {
+#pragma unroll
+      for (int i = 0; i < kPartBatch; ++i)
+        if (c0 + i < nc) q[i] = rp[c0 + i];
+      if (greedy) argmax_batch(q, c0, nc, m, idx);
+      else merge_batch(q, c0, nc, k2, m, s, x);
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
+  // position p = lane: target row p is this lane's, draft row p is lane D + 1 + p's
+  const int dl = min(D + 1 + lane, 63);
+  const float md_l = __shfl(m, dl), sd_l = __shfl(s, dl), xd_l = __shfl(x, dl);
   // position p = lane: its test
   const int p = lane;
   bool rej = false;
@@ -521,20 +622,20 @@ __device__ __forceinline__ Outcome seq_outcome(const Params& P, int b, RowScratc
   float mt = 0.f, md = 0.f, lr = 0.f;
   if (p <= L) {
     if (greedy) {
-      g = __float_as_int(rs.s[p]);
-      if (p < L) rej = xs[p] != g;
+      g = idx;
+      if (p < L) rej = xl != g;
       if (write && P.dbg_argmax) P.dbg_argmax[size_t(b) * (D + 1) + p] = g;
     } else {
-      mt = rs.m[p];
-      const float lnt = logf(rs.s[p]);
+      mt = m;
+      const float lnt = logf(s);
       float lnd = 0.f;
       if (p < L) {
-        md = rs.m[D + 1 + p];
-        lnd = logf(rs.s[D + 1 + p]);
-        const float lp = (rs.x[p] - mt) / T - lnt;
-        const float lq = (rs.x[D + 1 + p] - md) / T - lnd;
+        md = md_l;
+        lnd = logf(sd_l);
+        const float lp = (x - mt) * iT - lnt;
+        const float lq = (xd_l - md) * iT - lnd;
         const float ratio = expf(lp - lq);
-        rej = !(P.uniforms[size_t(b) * (D + 1) + p] < fminf(1.f, ratio));
+        rej = !(ul < fminf(1.f, ratio));
         lr = __uint_as_float(__float_as_uint(lnt - lnd) | 1u);
         if (write && P.dbg_logpq) {
           P.dbg_logpq[(size_t(b) * D + p) * 2] = lp;
@@ -558,10 +659,11 @@ __device__ __forceinline__ Outcome seq_outcome(const Params& P, int b, RowScratc
   o.mt = __shfl(mt, j);
   o.md = __shfl(md, j);
   o.lnrho = __shfl(lr, j);
+  o.u = __shfl(ul, D);
   if (write) {
     if (lane <= D) {
       if (greedy) toks[lane] = lane <= j ? g : -1;
-      else if (lane < j) toks[lane] = xs[lane];
+      else if (lane < j) toks[lane] = xl;
       else if (lane > j) toks[lane] = -1;      // position j is written by the final draw
     }
     if (lane == 0) {
@@ -594,16 +696,46 @@ template <typename E>
 constexpr int kItemBlocks = kItemElems<E> / kFinBlock;
 
 // 2^(y / 256) = 2^(k / 256) * 2^(r / 256), k = rint(y), r = y - k in [-1/2, 1/2] (exact);
-// 2^(r / 256) = e^(r ln2 / 256) from its degree-4 Taylor polynomial in r (truncation below
-// 4e-17 relative); 2^(k / 256) = e2[k mod 256] * 2^(k div 256). Arguments far below zero give
-// 0 (the integer conversion saturates and ldexp underflows).
+// 1 / k!, k = 0..17 (k! is exact in a double up to 17!)
+struct InvFactorials {
+  double v[18];
+  constexpr InvFactorials() : v() {
+    double f = 1.0;
+    v[0] = 1.0;
+    for (int k = 1; k < 18; ++k) {
+      f *= k;
+      v[k] = 1.0 / f;
+    }
+  }
+};
+constexpr InvFactorials kInvFact;
+
+// The table e2[i] = 2^(i / 256), i = 0..255, in shared memory: e^x at x = i ln2 / 256 <= 0.7 from
+// its Taylor polynomial of degree 17 (truncation below 3e-18 relative), Horner form.
+__device__ inline void fill_e2(double* e2, int tid) {
+  constexpr double c = 0.0027076061740622863;          // ln2 / 256
+  for (int i = tid; i < 256; i += kThreads) {
+    const double x = double(i) * c;
+    double p = kInvFact.v[17];
+#pragma unroll
+    for (int k = 16; k >= 0; --k) p = fma(p, x, kInvFact.v[k]);
+    e2[i] = p;
+  }
+}
+
+// 2^(r / 256) = e^u with u = r ln2 / 256, |u| <= a = ln2 / 512, from a cubic: the Taylor cubic
+// with the u^4 term economised by the Chebyshev polynomial T4 (u^4 ~ a^2 u^2 - a^4 / 8, off by
+// at most a^4 / 8), relative error below 2e-14; 2^(k / 256) = e2[k mod 256] * 2^(k div 256).
+// Arguments far below zero give 0 (the integer conversion saturates and ldexp underflows).
 __device__ inline double exp2k(double y, const double* e2) {
   constexpr double c = 0.0027076061740622863;          // ln2 / 256
-  constexpr double p1 = c, p2 = c * c / 2, p3 = c * c * c / 6, p4 = c * c * c * c / 24;
+  constexpr double a2 = c * c / 4;                     // a^2
+  constexpr double q0 = 1.0 - a2 * a2 / 192, q1 = c, q2 = (0.5 + a2 / 24) * c * c,
+                   q3 = c * c * c / 6;
   const double kf = __builtin_rint(y);
   const double r = y - kf;
   const int k = int(kf);
-  const double p = fma(fma(fma(fma(r, p4, p3), r, p2), r, p1), r, 1.0);
+  const double p = fma(fma(fma(r, q3, q2), r, q1), r, q0);
   return ldexp(e2[k & 255] * p, k >> 8);
 }
 
@@ -629,7 +761,7 @@ __device__ inline Draw make_draw(const Params& P, int b, const Outcome& o, const
   w.residual = o.mode == kResidual;
   w.j = o.j;
   const double T = double(P.temperature[b]);
-  w.u = double(P.uniforms[size_t(b) * (P.D + 1) + P.D]);
+  w.u = double(o.u);
   w.lnrho = double(o.lnrho);
   const double mt = double(o.mt);
   const double md = double(o.md);
@@ -660,6 +792,21 @@ struct ItemRuns {
     }
   }
 };
+
+// Target runs, and draft runs when `both`, block by block (block 0's pair arrives first).
+template <typename E>
+__device__ __forceinline__ void load_item(ItemRuns<E>& t, ItemRuns<E>& d, const E* trow,
+                                          const E* drow, bool both, int a0, int V, int lane) {
+#pragma unroll
+  for (int k = 0; k < kItemBlocks<E>; ++k) {
+    const int a = a0 + kFinBlock * k + kFinPer * lane;
+    const int n = max(0, min(kFinPer, V - a));
+    if (n > 0) {
+      t.r[k].load(trow, a, n);
+      if (both) d.r[k].load(drow, a, n);
+    }
+  }
+}
 
 // Exact weight of element e of the runs: e_t when target_only, else max(0, e_t/S_t - e_d/S_d).
 template <typename E>
@@ -694,22 +841,29 @@ __device__ inline double item_exact_mass(const Params& P, const E* trow, const E
   return wave_sum(s);
 }
 
-// The last final-draw item of a sequence: exact normalisers, item masses, token (one wavefront).
-// Up to 64 items the item records are read once, one per lane; beyond, they are re-read per pass.
+// The pick of a sequence: exact normalisers, item masses, token (one wavefront). Up to 64 items
+// the item records are read once, one per lane (r); beyond, they are re-read per pass.
+// The item records of sequence b that one pass of 64 lanes holds (all of them up to 64 items):
+// lane l gets item l's.
+__device__ inline FinPart first_records(const Params& P, int b, int lane) {
+  FinPart r = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, INFINITY, -INFINITY};
+  if (P.nF <= 64 && lane < P.nF) {
+    const FinPart& q = P.fpart[size_t(b) * P.nF + lane];
+    r.st = q.st; r.sd = q.sd; r.at = q.at; r.ad = q.ad;
+    r.bt = q.bt; r.bd = q.bd; r.dmin = q.dmin; r.dmax = q.dmax;
+  }
+  return r;
+}
+
 template <typename E>
-__device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w, int lane) {
+__device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w, const FinPart& r,
+                                          int lane) {
   const int nF = P.nF;
   const FinPart* fp = P.fpart + size_t(b) * nF;
   double* xmass = P.fmass + size_t(b) * nF;          // exact item masses of the slow path
   const E* trow = final_row<E>(P, b, w.j, false);
   const E* drow = w.residual ? final_row<E>(P, b, w.j, true) : trow;
   const bool one = nF <= 64;
-  FinPart r = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, INFINITY, -INFINITY};
-  if (one && lane < nF) {
-    const FinPart& q = fp[lane];
-    r.st = q.st; r.sd = q.sd; r.at = q.at; r.ad = q.ad;
-    r.bt = q.bt; r.bd = q.bd; r.dmin = q.dmin; r.dmax = q.dmax;
-  }
   // the record of item f (f = lane + 64 k, this lane's)
   auto rec = [&](int f) {
     if (one) return r;
@@ -735,7 +889,8 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
   const double it = 1.0 / st, id = 1.0 / sd;
   // did the band hold the exact ratio (with room for the rounding of its bounds), and is every
   // item's in-band set one ratio class?
-  const bool slow = w.residual && (__any(multi) || !(fabs(log(st / sd) - w.lnrho) < 0.5 * kBand));
+  const bool slow = w.residual &&
+                    (__any(multi) || !(fabsf(logf(float(st / sd)) - float(w.lnrho)) < 0.5f * float(kBand)));
   if (slow) {
     for (int f = 0; f < nF; ++f) {
       const double m = item_exact_mass<E>(P, trow, drow, w, f, false, it, id, lane);
@@ -756,30 +911,51 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
   };
 
   // Z, then the first item whose inclusive prefix exceeds t = u Z (else the last item with
-  // positive mass), 64 items at a time
-  double Z = 0.0;
-  for (int base = 0; base < nF; base += 64) Z += wave_total(mass(base + lane));
-  if (!(Z > 0.0) && !target_only) {
-    target_only = true;                // residual of zero mass (rounding only): draw from p_j
-    Z = 0.0;
-    for (int base = 0; base < nF; base += 64) Z += wave_total(mass(base + lane));
-  }
-  const double t = w.u * Z;
+  // positive mass), 64 items at a time (up to 64 items: one scan gives both)
+  double Z = 0.0, t = 0.0;
   int fstar = -1, flast = -1;
-  double run = 0.0, total = 0.0;
-  for (int base = 0; base < nF && fstar < 0; base += 64) {
-    const int f = base + lane;
-    const double m = mass(f);
-    const double inc = dpp_scan_add(m) + total;
-    const unsigned long long over = __ballot(f < nF && inc > t);
-    const unsigned long long pos = __ballot(f < nF && m > 0.0);
-    if (pos) flast = base + 63 - __builtin_clzll(pos);
-    if (over) {
-      const int l = __builtin_ctzll(over);
-      fstar = base + l;
-      run = readlane(inc - m, l);
+  double run = 0.0;
+  if (one) {
+    double m = mass(lane);
+    double inc = dpp_scan_add(m);
+    Z = readlane(inc, 63);
+    if (!(Z > 0.0) && !target_only) {
+      target_only = true;              // residual of zero mass (rounding only): draw from p_j
+      m = mass(lane);
+      inc = dpp_scan_add(m);
+      Z = readlane(inc, 63);
     }
-    total = readlane(inc, 63);
+    t = w.u * Z;
+    const unsigned long long over = __ballot(lane < nF && inc > t);
+    const unsigned long long pos = __ballot(lane < nF && m > 0.0);
+    if (pos) flast = 63 - __builtin_clzll(pos);
+    if (over) {
+      fstar = __builtin_ctzll(over);
+      run = readlane(inc - m, fstar);
+    }
+  } else {
+    for (int base = 0; base < nF; base += 64) Z += wave_total(mass(base + lane));
+    if (!(Z > 0.0) && !target_only) {
+      target_only = true;
+      Z = 0.0;
+      for (int base = 0; base < nF; base += 64) Z += wave_total(mass(base + lane));
+    }
+    t = w.u * Z;
+    double total = 0.0;
+    for (int base = 0; base < nF && fstar < 0; base += 64) {
+      const int f = base + lane;
+      const double m = mass(f);
+      const double inc = dpp_scan_add(m) + total;
+      const unsigned long long over = __ballot(f < nF && inc > t);
+      const unsigned long long pos = __ballot(f < nF && m > 0.0);
+      if (pos) flast = base + 63 - __builtin_clzll(pos);
+      if (over) {
+        const int l = __builtin_ctzll(over);
+        fstar = base + l;
+        run = readlane(inc - m, l);
+      }
+      total = readlane(inc, 63);
+    }
   }
   const bool past_end = fstar < 0;
   int32_t* out = P.out_tokens + size_t(b) * (P.D + 1) + w.j;
@@ -796,8 +972,7 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
   // holding t is rescanned, else every block in order.
   const int a0 = fstar * kItemElems<E>;
   ItemRuns<E> tr, dr;
-  tr.load(trow, a0, P.V, lane);
-  if (!target_only) dr.load(drow, a0, P.V, lane);
+  load_item<E>(tr, dr, trow, drow, !target_only, a0, P.V, lane);
   constexpr int KB = kItemBlocks<E>;
   const FinPart* rf = fp + fstar;
   const bool bonus = !w.residual;
@@ -823,13 +998,14 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
     if (found < 0 && k >= kfirst && k <= klast) {     // wave-uniform
       const int a = a0 + kFinBlock * k + kFinPer * lane;
       const int n = max(0, min(kFinPer, P.V - a));
-      double ls = 0.0;
+      double ls = 0.0, wts[kFinPer];
 #pragma unroll
       for (int e = 0; e < kFinPer; ++e) {
+        wts[e] = 0.0;
         if (e < n) {
-          const double wt = exact_weight<E>(tr.r[k], dr.r[k], e, w, target_only, it, id);
-          ls += wt;
-          if (wt > 0.0) last_pos = a + e;
+          wts[e] = exact_weight<E>(tr.r[k], dr.r[k], e, w, target_only, it, id);
+          ls += wts[e];
+          if (wts[e] > 0.0) last_pos = a + e;
         }
       }
       const double inc = dpp_scan_add(ls) + run;
@@ -846,9 +1022,8 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
 #pragma unroll
           for (int e = 0; e < kFinPer; ++e) {
             if (e < n && k2 < 0) {
-              const double wt = exact_weight<E>(tr.r[k], dr.r[k], e, w, target_only, it, id);
-              acc += wt;
-              if (wt > 0.0) my_last = a + e;
+              acc += wts[e];
+              if (wts[e] > 0.0) my_last = a + e;
               if (acc > t) k2 = a + e;
             }
           }
@@ -859,8 +1034,10 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
       run = readlane(inc, 63);
     }
   }
-  // rounding put u * Z past the end: the last element with positive weight
-  for (int off = 32; off > 0; off >>= 1) last_pos = max(last_pos, __shfl_xor(last_pos, off));
+  if (found < 0) {                     // rounding put u * Z past the end: the last element
+    for (int off = 32; off > 0; off >>= 1)   // with positive weight
+      last_pos = max(last_pos, __shfl_xor(last_pos, off));
+  }
   if (lane == 0) *out = (found >= 0) ? found : last_pos;
 }
 
@@ -889,44 +1066,71 @@ __device__ __forceinline__ bool item_sweep(const Params& P, int a0, const Draw& 
           sd += ed;
           // x_t - x_d against the band: above it the element is certainly in the positive part
           const double dx = xt - xd;
-          const double above = dx > w.dhi ? 1.0 : 0.0;
+          const bool le = dx <= w.dhi;
+          const double above = le ? 0.0 : 1.0;
           kat[k] = fma(above, et, kat[k]);
           kad[k] = fma(above, ed, kad[k]);
-          band |= int(dx <= w.dhi) & int(dx >= w.dlo);     // no branch per element
+          band |= int(le) & int(dx >= w.dlo);               // no branch per element
         } else {
           kat[k] += et;
         }
       }
     }
+    // blocks in order: block k + 1's data is not touched before block k is summed, so the
+    // wavefront starts on a block as soon as its loads have landed
+    __builtin_amdgcn_sched_barrier(0);
   }
   return band != 0;
 }
 
-// fp64 partial sums of item f of sequence b from the lane's runs, stored to the item's record
-// (no wait). The rare elements inside the band are summed by a second sweep, taken only by
+// fp64 partial sums of item f of sequence b (the lane loads its runs), stored to the item's
+// record. The rare elements inside the band are summed by a second sweep, taken only by
 // wavefronts that have some.
 template <typename E>
 __device__ __forceinline__ void item_sums(const Params& P, int b, int f, const Draw& w,
-                                          const ItemRuns<E>& tr, const ItemRuns<E>& dr,
                                           int lane) {
   constexpr int KB = kItemBlocks<E>;
   const int a0 = f * kItemElems<E>;
-  const bool full = a0 + kItemElems<E> <= P.V;
+  const E* trow = final_row<E>(P, b, w.j, false);
+  const E* drow = final_row<E>(P, b, w.j, true);
+  // Items of full length whose rows are 16-byte aligned load with straight-line vector loads,
+  // block by block, so that the sweep of a block waits only for that block's data.
+  const uintptr_t bases = reinterpret_cast<uintptr_t>(trow) |
+                          (w.residual ? reinterpret_cast<uintptr_t>(drow) : uintptr_t(0));
+  const bool fast = a0 + kItemElems<E> <= P.V && (bases & 15) == 0;
   double st = 0, sd = 0, bt = 0, bd = 0, dmin = INFINITY, dmax = -INFINITY;
   double kat[KB], kad[KB];
 #pragma unroll
   for (int k = 0; k < KB; ++k) kat[k] = kad[k] = 0.0;
   bool band;
+  ItemRuns<E> tr, dr;
   if (w.residual) {
-    band = full ? item_sweep<E, true, true>(P, a0, w, tr, dr, lane, st, sd, kat, kad)
-                : item_sweep<E, false, true>(P, a0, w, tr, dr, lane, st, sd, kat, kad);
+    if (fast) {
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int a = a0 + kFinBlock * k + kFinPer * lane;
+        tr.r[k].load_vec(trow + a);
+        dr.r[k].load_vec(drow + a);
+      }
+      __builtin_amdgcn_sched_barrier(0);          // every load issued before the sweep
+      band = item_sweep<E, true, true>(P, a0, w, tr, dr, lane, st, sd, kat, kad);
+    } else {
+      load_item<E>(tr, dr, trow, drow, true, a0, P.V, lane);
+      band = item_sweep<E, false, true>(P, a0, w, tr, dr, lane, st, sd, kat, kad);
+    }
   } else {
-    band = full ? item_sweep<E, true, false>(P, a0, w, tr, dr, lane, st, sd, kat, kad)
-                : item_sweep<E, false, false>(P, a0, w, tr, dr, lane, st, sd, kat, kad);
+    if (fast) {
+#pragma unroll
+      for (int k = 0; k < KB; ++k) tr.r[k].load_vec(trow + a0 + kFinBlock * k + kFinPer * lane);
+      __builtin_amdgcn_sched_barrier(0);
+      band = item_sweep<E, true, false>(P, a0, w, tr, dr, lane, st, sd, kat, kad);
+    } else {
+      load_item<E>(tr, dr, trow, drow, false, a0, P.V, lane);
+      band = item_sweep<E, false, false>(P, a0, w, tr, dr, lane, st, sd, kat, kad);
+    }
   }
-  if (__any(band)) {                   // rare: reload the item and sum its in-band elements
-    const E* trow = final_row<E>(P, b, w.j, false);
-    const E* drow = final_row<E>(P, b, w.j, true);
+  const bool any_band = __any(band);
+  if (any_band) {                      // rare: reload the item and sum its in-band elements
     for (int k = 0; k < KB; ++k) {
       const int a = a0 + kFinBlock * k + kFinPer * lane;
       const int n = max(0, min(kFinPer, P.V - a));
@@ -954,10 +1158,12 @@ __device__ __forceinline__ void item_sums(const Params& P, int b, int f, const D
   if (w.residual) {
     st = dpp_scan(st, 0.0, add);
     sd = dpp_scan(sd, 0.0, add);
-    bt = dpp_scan(bt, 0.0, add);
-    bd = dpp_scan(bd, 0.0, add);
-    dmin = dpp_scan(dmin, INFINITY, mn);
-    dmax = dpp_scan(dmax, -INFINITY, mx);
+    if (any_band) {                    // else every lane holds the identities already
+      bt = dpp_scan(bt, 0.0, add);
+      bd = dpp_scan(bd, 0.0, add);
+      dmin = dpp_scan(dmin, INFINITY, mn);
+      dmax = dpp_scan(dmax, -INFINITY, mx);
+    }
   }
   if (lane == 63) {                    // plain stores: the pick kernel runs after this kernel
     double at = 0.0, ad = 0.0, et = 0.0;
@@ -1010,33 +1216,29 @@ __device__ __forceinline__ void row_workgroup(const Params& P, Shared& sm, int r
     row_chunk<E>(P, sm, b, p, which, c, L, T, greedy, tid);
 }
 
-// Final-draw item wavefront: item g = b * nF + f (wave-uniform), after the row kernel. Item 0
-// of each sequence writes the sequence's outcome.
+// Final-draw item wavefront: item g = b * nF + f < B nF (wave-uniform), after the row kernel,
+// with the outcome's inputs loaded. Item 0 of each sequence writes the sequence's outcome.
 template <typename E>
-__device__ __forceinline__ void item_wavefront(const Params& P, const double* e2, RowScratch& rs,
-                                               int g, int lane) {
-  if (g >= P.B * P.nF) return;
+__device__ __forceinline__ void item_wavefront(const Params& P, const double* e2, int g,
+                                               const OutcomeIn& in, int lane) {
   const int b = g / P.nF;
   const int f = g - b * P.nF;
-  const Outcome o = seq_outcome<E>(P, b, rs, lane, f == 0);
+  const Outcome o = seq_outcome<E>(P, b, in, lane, f == 0);
   if (o.mode != kResidual && o.mode != kBonus) return;   // no draw (greedy or invalid)
-  const Draw w = make_draw(P, b, o, e2);
-  ItemRuns<E> tr, dr;
-  tr.load(final_row<E>(P, b, w.j, false), f * kItemElems<E>, P.V, lane);
-  if (w.residual) dr.load(final_row<E>(P, b, w.j, true), f * kItemElems<E>, P.V, lane);
-  item_sums<E>(P, b, f, w, tr, dr, lane);
+  item_sums<E>(P, b, f, make_draw(P, b, o, e2), lane);
 }
 
-// Pick wavefront of sequence b, after every item is stored.
+// Pick wavefront of sequence b < B, after every item is stored, with its first item records r
+// and outcome words (a, c) loaded.
 template <typename E>
-__device__ __forceinline__ void pick_wavefront(const Params& P, const double* e2, int b, int lane) {
-  if (b >= P.B) return;
-  const unsigned long long a = uniform64(P.pub[b].a);
-  const unsigned long long c = uniform64(P.pub[b].c);
+__device__ __forceinline__ void pick_wavefront(const Params& P, const double* e2, int b,
+                                               const FinPart& r, unsigned long long a,
+                                               unsigned long long c, int lane) {
   if (!draw_ready(a, c)) return;
   const Outcome o = {unsigned(a & 3u), int((a >> 2) & 31u), __uint_as_float(unsigned(a >> 32)),
-                     __uint_as_float(unsigned(c)), __uint_as_float(unsigned(c >> 32))};
-  wave_pick<E>(P, b, make_draw(P, b, o, e2), lane);
+                     __uint_as_float(unsigned(c)), __uint_as_float(unsigned(c >> 32)),
+                     P.uniforms[size_t(b) * (P.D + 1) + P.D]};
+  wave_pick<E>(P, b, make_draw(P, b, o, e2), r, lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1051,24 +1253,32 @@ __global__ __launch_bounds__(kThreads) void row_kernel(Params P) {
 
 // Final-draw kernels, after the row kernel: outcome and partial sums (one wavefront per item),
 // then the pick (one wavefront per sequence).
+// Each wavefront issues its first loads before the workgroup fills the e2 table.
 template <typename E>
 __global__ __launch_bounds__(kThreads) void item_kernel(Params P) {
   __shared__ double e2[256];
-  __shared__ RowScratch rs[kWaves];
-  const int tid = threadIdx.x;
-  for (int i = tid; i < 256; i += kThreads) e2[i] = exp2(double(i) / 256.0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int g = int(blockIdx.x) * kWaves + uniform(tid >> 6);
+  const bool live = g < P.B * P.nF;
+  const OutcomeIn in = load_outcome(P, live ? g / P.nF : 0, lane);
+  fill_e2(e2, tid);
   __syncthreads();
-  const int wave = uniform(tid >> 6);
-  item_wavefront<E>(P, e2, rs[wave], int(blockIdx.x) * kWaves + wave, tid & 63);
+  if (live) item_wavefront<E>(P, e2, g, in, lane);
 }
 
 template <typename E>
 __global__ __launch_bounds__(kThreads) void pick_kernel(Params P) {
   __shared__ double e2[256];
-  const int tid = threadIdx.x;
-  for (int i = tid; i < 256; i += kThreads) e2[i] = exp2(double(i) / 256.0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int b = int(blockIdx.x) * kWaves + uniform(tid >> 6);
+  const bool live = b < P.B;
+  const int bl = live ? b : 0;
+  const FinPart r = first_records(P, bl, lane);
+  const unsigned long long a = uniform64(P.pub[bl].a);
+  const unsigned long long c = uniform64(P.pub[bl].c);
+  fill_e2(e2, tid);
   __syncthreads();
-  pick_wavefront<E>(P, e2, int(blockIdx.x) * kWaves + uniform(tid >> 6), tid & 63);
+  if (live) pick_wavefront<E>(P, e2, b, r, a, c, lane);
 }
 
 // ------------------------------------------------------------------------------------------

@@ -208,3 +208,26 @@ def test_workspace_reuse_across_batch_sizes():
         for wsp in (None, ws):
             al, toks = G.run(w, workspace=wsp)
             G.compare(ref, al, toks, f"B={B} caller_ws={wsp is not None}")
+
+
+def test_bf16_logits_beyond_the_packed_max_range():
+    """bf16 logits of magnitude 2^121 and above sit on fp16's inf / NaN bit patterns, where the
+    packed row maximum does not order them; chunks holding them are redone with exact maxima.
+    Sampled rows (T = 1 and 0.7) get such values at seeded places, including rows that decide
+    the accept tests and the final draw."""
+    w = make("c3", 3, B=16, V=20011)
+    rng = np.random.default_rng(77)
+    # bf16 bit patterns: +2^121 (fp16 +inf), +2^122 (fp16 signalling NaN), -2^122, 1.5 * 2^125
+    # (fp16 quiet NaN), -1.5 * 2^125
+    # Target rows of sequences 0-7 and draft rows of 8-15 only: where both p(x) and q(x) lie
+    # some 1e36 below their rows' maxima, log p(x) - log q(x) is lost to cancellation on both
+    # sides and no answer is defined.
+    huge = np.array([0x7C00, 0x7C80, 0xFC80, 0x7E40, 0xFE40], np.uint16)
+    for arr, rows, seqs in ((w.target, w.D + 1, range(0, 8)), (w.draft, w.D, range(8, 16))):
+        for _ in range(12):
+            b, r, v = rng.choice(list(seqs)), rng.integers(rows), rng.integers(w.V)
+            arr[b, r, v] = huge[rng.integers(huge.size)]
+    w.temperature[::2] = 0.7
+    ref = verify_workload(w)
+    al, toks = G.run(w)
+    G.compare(ref, al, toks, "huge bf16 logits")

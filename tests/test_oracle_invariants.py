@@ -137,3 +137,17 @@ def test_flag_rate_estimator_is_small_on_full_headline_config():
     r = verify_workload(w)
     assert r.flag_measure.mean() < 1e-4
     assert 1.8 < r.accept_len.mean() < 4.0
+
+
+def test_ratio_beyond_the_double_range_accepts():
+    """q(x) far below p(x) (log-ratio 1500): q <= p, so the draft is accepted whatever the
+    uniform (step 1 of the rule, SD recap), and the call is then a bonus draw from p_1."""
+    V = 4
+    target = np.zeros((1, 2, V), np.float32)
+    draft = np.zeros((1, 1, V), np.float32)
+    draft[0, 0, 1] = 1500.0                       # q(0) ~ exp(-1500), p(0) = 1/4
+    tokens = np.array([[0]], np.int32)
+    u = np.array([[0.999999, 0.3]], np.float32)
+    r = verify(target, draft, tokens, None, u, np.ones(1, np.float32))
+    assert r.accept_len[0] == 2 and r.tokens[0, 0] == 0
+    assert r.tokens[0, 1] == 1                    # inverse CDF of uniform p at 0.3: bin 1
