@@ -1253,32 +1253,32 @@ __global__ __launch_bounds__(kThreads) void row_kernel(Params P) {
 
 // Final-draw kernels, after the row kernel: outcome and partial sums (one wavefront per item),
 // then the pick (one wavefront per sequence).
-// Each wavefront issues its first loads before the workgroup fills the e2 table.
+// The e2 table is filled first (the workgroup barrier would otherwise wait for every load
+// issued before it).
 template <typename E>
 __global__ __launch_bounds__(kThreads) void item_kernel(Params P) {
   __shared__ double e2[256];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int g = int(blockIdx.x) * kWaves + uniform(tid >> 6);
-  const bool live = g < P.B * P.nF;
-  const OutcomeIn in = load_outcome(P, live ? g / P.nF : 0, lane);
   fill_e2(e2, tid);
   __syncthreads();
-  if (live) item_wavefront<E>(P, e2, g, in, lane);
+  const int g = int(blockIdx.x) * kWaves + uniform(tid >> 6);
+  if (g >= P.B * P.nF) return;
+  const OutcomeIn in = load_outcome(P, g / P.nF, lane);
+  item_wavefront<E>(P, e2, g, in, lane);
 }
 
 template <typename E>
 __global__ __launch_bounds__(kThreads) void pick_kernel(Params P) {
   __shared__ double e2[256];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int b = int(blockIdx.x) * kWaves + uniform(tid >> 6);
-  const bool live = b < P.B;
-  const int bl = live ? b : 0;
-  const FinPart r = first_records(P, bl, lane);
-  const unsigned long long a = uniform64(P.pub[bl].a);
-  const unsigned long long c = uniform64(P.pub[bl].c);
   fill_e2(e2, tid);
   __syncthreads();
-  if (live) pick_wavefront<E>(P, e2, b, r, a, c, lane);
+  const int b = int(blockIdx.x) * kWaves + uniform(tid >> 6);
+  if (b >= P.B) return;
+  const FinPart r = first_records(P, b, lane);
+  const unsigned long long a = uniform64(P.pub[b].a);
+  const unsigned long long c = uniform64(P.pub[b].c);
+  pick_wavefront<E>(P, e2, b, r, a, c, lane);
 }
 
 // ------------------------------------------------------------------------------------------
