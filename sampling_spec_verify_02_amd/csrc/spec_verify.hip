@@ -55,7 +55,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // few 1e-6, so the exact ln(S_t/S_d) lies well inside; the pick checks that it does.
 constexpr double kBand = 3e-5;
 
-// state of a sequence's outcome, as published to the final draw (0: not decided)
+// kind of a sequence's final token, in its outcome words
 enum Mode : unsigned { kNoDraw = 1, kResidual = 2, kBonus = 3 };
 
 struct RowPart {      // partial statistics of one row chunk
@@ -694,6 +694,8 @@ template <typename E>
 constexpr int kItemElems = kRowChunkBytes / int(sizeof(E)) / kItemsPerChunk;
 template <typename E>
 constexpr int kItemBlocks = kItemElems<E> / kFinBlock;
+static_assert(kItemBlocks<uint16_t> <= kMaxItemBlocks && kItemBlocks<float> <= kMaxItemBlocks,
+              "an item record holds the masses of at most kMaxItemBlocks blocks");
 
 // 2^(y / 256) = 2^(k / 256) * 2^(r / 256), k = rint(y), r = y - k in [-1/2, 1/2] (exact);
 // 1 / k!, k = 0..17 (k! is exact in a double up to 17!)
