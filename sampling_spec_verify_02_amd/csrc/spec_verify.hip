@@ -9,8 +9,8 @@
 // Three kernels per call, in stream order; each hands its results to the next through the
 // kernel boundary, so no kernel waits for another workgroup and none uses atomics.
 //
-// * Row kernel: one workgroup per 32 KB chunk of a row, position-major order (all position-0
-//   rows of the batch first, then position 1, ...). It streams its chunk with non-temporal
+// * Row kernel: one workgroup per 32 KB chunk of a row, position-major order (the position-0
+//   target rows of the batch, then its position-0 draft rows, then position 1, ...). It streams its chunk with non-temporal
 //   16-byte loads and stores the chunk's exact max and fp32 sum exp((x - max) / T) (sampled
 //   rows) or max and lowest argmax (greedy target rows); the chunk holding the draft token x_p
 //   also records the logit at x_p. Rows the method does not need (padding, draft rows of greedy
@@ -128,6 +128,12 @@ __device__ inline void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "me
 // ------------------------------------------------------------------------------------------
 // element access
 
+// A load from global memory through a generic pointer (a global, not a flat, access).
+template <typename T>
+__device__ inline T ld_global(const T* p) {
+  return *(__attribute__((address_space(1))) const T*)p;
+}
+
 template <typename E> struct Elem;
 // Running maximum of packed values. bf16 pairs are compared as fp16 pairs (one packed max per
 // word): both formats are sign-magnitude with the magnitude ordered like its bit pattern, so
@@ -144,7 +150,7 @@ __device__ inline uint32_t pk_max_bf16(uint32_t a, uint32_t b) {
 template <> struct Elem<uint16_t> {          // bf16 bit patterns
   static constexpr int kVec = 8;             // elements per 16-byte load
   __device__ static float get(const uint16_t* p, size_t i) {
-    return __uint_as_float(uint32_t(p[i]) << 16);
+    return __uint_as_float(uint32_t(ld_global(p + i)) << 16);
   }
   __device__ static float lane(const uint4& v, int e) {
     const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
@@ -164,7 +170,7 @@ template <> struct Elem<uint16_t> {          // bf16 bit patterns
 };
 template <> struct Elem<float> {
   static constexpr int kVec = 4;
-  __device__ static float get(const float* p, size_t i) { return p[i]; }
+  __device__ static float get(const float* p, size_t i) { return ld_global(p + i); }
   __device__ static float lane(const uint4& v, int e) {
     return __uint_as_float(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
   }
@@ -179,9 +185,12 @@ template <> struct Elem<float> {
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
 
+// Non-temporal 16-byte load. The logits are global memory; saying so makes it a global (not a
+// flat) load, which counts against the vector-memory counter only.
 __device__ inline uint4 load_stream(const uint4* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  const u32x4 v = __builtin_nontemporal_load((global_u32x4*)p);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -1203,11 +1212,13 @@ __device__ inline bool draw_ready(unsigned long long a, unsigned long long c) {
 template <typename E>
 __device__ __forceinline__ void row_workgroup(const Params& P, Shared& sm, int rid, int tid) {
   const int nc = P.nchunk;
+  // position-major; within a position the target rows of every sequence, then the draft rows
+  // (measured faster than alternating target and draft rows per sequence)
   const int per_p = P.B * 2 * nc;
   const int p = rid / per_p;
   const int local = rid - p * per_p;
-  const int b = local / (2 * nc);
-  const int which = (local % (2 * nc)) / nc;          // 0 target row p, 1 draft row p
+  const int which = local / (P.B * nc);               // 0 target row p, 1 draft row p
+  const int b = (local / nc) % P.B;
   const int c = local % nc;
   const int D = P.D;
   const int L = P.lens ? P.lens[b] : D;
