@@ -50,6 +50,7 @@ constexpr int kFinPer = 8;                    // consecutive elements per lane a
 constexpr int kFinBlock = 64 * kFinPer;       // elements per wavefront block (512)
 constexpr int kItemsPerChunk = 8;             // final-draw items per row chunk length
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 // Half-width of the band (in ln(e_t/e_d)) inside which an element's sign in max(0, p - q) is
 // not decided from the fp32 estimate of ln(S_t/S_d). The fp32 statistics are accurate to a
 // few 1e-6, so the exact ln(S_t/S_d) lies well inside; the pick checks that it does.
@@ -310,6 +311,11 @@ __device__ inline void wave_am(float& v, int& i) {
     am_combine(v, i, v2, i2);
   }
 }
+
+// Natural log and exp from the hardware base-2 instructions (relative error near 1e-7; the
+// accept tests and the band around ln(S_t / S_d) need 1e-5).
+__device__ inline float ln_hw(float x) { return __builtin_amdgcn_logf(x) * kLn2; }
+__device__ inline float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 
 // ms_combine without branches, for operands that are either empty (m = -inf, s = 0) or
 // non-empty (s > 0); the same result for (a, b) as for (b, a).
@@ -636,14 +642,14 @@ __device__ __forceinline__ Outcome seq_outcome(const Params& P, int b, const Out
       if (write && P.dbg_argmax) P.dbg_argmax[size_t(b) * (D + 1) + p] = g;
     } else {
       mt = m;
-      const float lnt = logf(s);
+      const float lnt = ln_hw(s);
       float lnd = 0.f;
       if (p < L) {
         md = md_l;
-        lnd = logf(sd_l);
+        lnd = ln_hw(sd_l);
         const float lp = (x - mt) * iT - lnt;
         const float lq = (xd_l - md) * iT - lnd;
-        const float ratio = expf(lp - lq);
+        const float ratio = exp_hw(lp - lq);
         rej = !(ul < fminf(1.f, ratio));
         lr = __uint_as_float(__float_as_uint(lnt - lnd) | 1u);
         if (write && P.dbg_logpq) {
@@ -901,7 +907,7 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
   // did the band hold the exact ratio (with room for the rounding of its bounds), and is every
   // item's in-band set one ratio class?
   const bool slow = w.residual &&
-                    (__any(multi) || !(fabsf(logf(float(st / sd)) - float(w.lnrho)) < 0.5f * float(kBand)));
+                    (__any(multi) || !(fabsf(ln_hw(float(st / sd)) - float(w.lnrho)) < 0.5f * float(kBand)));
   if (slow) {
     for (int f = 0; f < nF; ++f) {
       const double m = item_exact_mass<E>(P, trow, drow, w, f, false, it, id, lane);
