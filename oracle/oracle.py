@@ -36,7 +36,10 @@ x_0..x_{L-1} and uniforms u[b][0..D]:
 
 Boundary flags (decisions that rounding may legitimately flip): an accept test is flagged when
 |u - r| < 1e-5 (r = p(x)/q(x), unclamped); a sampled final draw is flagged when u_f * Z lies
-within 1e-5 * w_k of either edge of the chosen token's bin [F_{k-1}, F_k).
+within 1e-5 * w_k of either edge of the chosen token's bin [F_{k-1}, F_k); a residual draw is
+flagged when its mass Z = sum max(0, p - q) is below 1e-9: its weights are then differences of
+nearly equal probabilities, which fp64 evaluations of p and q carry with absolute errors of
+1e-15 or more per token, so the rounding decides where the mass lies.
 """
 from __future__ import annotations
 
@@ -46,6 +49,7 @@ import math
 import numpy as np
 
 FLAG_TOL = 1e-5
+RESIDUAL_MIN_MASS = 1e-9
 
 
 @dataclasses.dataclass
@@ -206,6 +210,9 @@ def verify(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray,
         if rejected_at >= 0:
             j = rejected_at
             w = residual_weights(softmax(target[b, j], T), softmax(draft[b, j], T))
+            if w.sum() < RESIDUAL_MIN_MASS:   # mass below what fp64 resolves in p - q
+                res.flagged[b] = True
+                res.flag_measure[b] += 1.0
             if not np.any(w > 0):
                 w = softmax(target[b, j], T)
             res.final_mode[b] = 2

@@ -231,3 +231,33 @@ def test_bf16_logits_beyond_the_packed_max_range():
     ref = verify_workload(w)
     al, toks = G.run(w)
     G.compare(ref, al, toks, "huge bf16 logits")
+
+
+def test_maximum_draft_length():
+    """D = 31, the largest the boundary accepts: 63 rows per sequence, one lane each in the
+    outcome."""
+    w = make("c5", 12, B=24, V=5003, D=31)
+    ref = verify_workload(w)
+    al, toks = G.run(w)
+    G.compare(ref, al, toks, "D=31")
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 300007), ("f32", 200003)])
+def test_large_vocabularies(dtype, V):
+    """More than eight 32 KB chunks per row: the outcome merges the chunk partials in several
+    batches."""
+    w = make("c3" if dtype == "bf16" else "c2", 13, B=6, V=V)
+    ref = verify_workload(w)
+    al, toks = G.run(w)
+    G.compare(ref, al, toks, f"{dtype} V={V}")
+
+
+@pytest.mark.parametrize("T", [1e-3, 0.05, 10.0, 1000.0])
+def test_temperature_extremes(T):
+    """Near-greedy and near-uniform sampling: exponent ranges of the fp32 row sums and of the
+    fp64 final-draw weights far from the headline's."""
+    w = make("c3", 14, B=16, V=20011)
+    w.temperature[:] = np.float32(T)
+    ref = verify_workload(w)
+    al, toks = G.run(w)
+    G.compare(ref, al, toks, f"T={T}")

@@ -151,3 +151,19 @@ def test_ratio_beyond_the_double_range_accepts():
     r = verify(target, draft, tokens, None, u, np.ones(1, np.float32))
     assert r.accept_len[0] == 2 and r.tokens[0, 0] == 0
     assert r.tokens[0, 1] == 1                    # inverse CDF of uniform p at 0.3: bin 1
+
+
+def test_residual_below_fp64_resolution_is_flagged():
+    """A rejection where p and q agree except far out in the tail: the residual mass is about
+    1e-12, made of differences of probabilities near 1/2, so the draw is left to rounding and
+    the row is flagged. The same shape with a clear difference is not flagged."""
+    target = np.array([[[0.0, -4e-12, -50.0], [0.0, 0.0, 0.0]]], np.float64)
+    draft = np.array([[[0.0, 0.0, -40.0]]], np.float64)
+    tokens = np.array([[2]], np.int32)
+    u = np.array([[0.5, 0.3]], np.float32)
+    r = verify(target, draft, tokens, None, u, np.ones(1, np.float32))
+    assert r.accept_len[0] == 1 and r.final_mode[0] == 2      # q(2) = e^10 p(2): rejected
+    assert r.flagged[0]
+    target[0, 0, 1] = -0.5                                    # residual mass about 0.12
+    r = verify(target, draft, tokens, None, u, np.ones(1, np.float32))
+    assert r.accept_len[0] == 1 and not r.flagged[0] and r.tokens[0, 0] == 0
