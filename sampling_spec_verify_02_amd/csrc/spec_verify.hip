@@ -1235,14 +1235,11 @@ __device__ __forceinline__ void row_workgroup(const Params& P, Shared& sm, int r
     row_chunk<E>(P, sm, b, p, which, c, L, T, greedy, tid);
 }
 
-// Final-draw item wavefront: item g = b * nF + f < B nF (wave-uniform), after the row kernel,
-// with the outcome's inputs loaded. Item 0 of each sequence writes the sequence's outcome.
+// Final-draw item wavefront: item f of sequence b (wave-uniform), after the row kernel, given
+// the sequence's outcome.
 template <typename E>
-__device__ __forceinline__ void item_wavefront(const Params& P, const double* e2, int g,
-                                               const OutcomeIn& in, int lane) {
-  const int b = g / P.nF;
-  const int f = g - b * P.nF;
-  const Outcome o = seq_outcome<E>(P, b, in, lane, f == 0);
+__device__ __forceinline__ void item_wavefront(const Params& P, const double* e2, int b, int f,
+                                               const Outcome& o, int lane) {
   if (o.mode != kResidual && o.mode != kBonus) return;   // no draw (greedy or invalid)
   item_sums<E>(P, b, f, make_draw(P, b, o, e2), lane);
 }
@@ -1272,18 +1269,34 @@ __global__ __launch_bounds__(kThreads) void row_kernel(Params P) {
 
 // Final-draw kernels, after the row kernel: outcome and partial sums (one wavefront per item),
 // then the pick (one wavefront per sequence).
-// The e2 table is filled first (the workgroup barrier would otherwise wait for every load
-// issued before it).
+// Item kernel: the kWaves wavefronts of a workgroup take consecutive items of one sequence
+// (items per sequence rounded up to a multiple of kWaves; the extra ones do nothing).
+// Wavefront 0 derives the sequence's outcome (and, for the sequence's first workgroup, writes
+// it) while the others fill the e2 table; the outcome reaches them through LDS.
 template <typename E>
 __global__ __launch_bounds__(kThreads) void item_kernel(Params P) {
   __shared__ double e2[256];
+  __shared__ Outcome so;
   const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int per_seq = (P.nF + kWaves - 1) / kWaves;      // workgroups per sequence
+  const int b = int(blockIdx.x) / per_seq;
+  const int f = (int(blockIdx.x) - b * per_seq) * kWaves + wave;
+  if (wave == 0) {
+    const OutcomeIn in = load_outcome(P, b, lane);
+    const Outcome o = seq_outcome<E>(P, b, in, lane, f == 0);
+    if (lane == 0) so = o;
+  }
   fill_e2(e2, tid);
   __syncthreads();
-  const int g = int(blockIdx.x) * kWaves + uniform(tid >> 6);
-  if (g >= P.B * P.nF) return;
-  const OutcomeIn in = load_outcome(P, g / P.nF, lane);
-  item_wavefront<E>(P, e2, g, in, lane);
+  Outcome o;                           // wave-uniform copies of the shared words
+  o.mode = unsigned(uniform(int(so.mode)));
+  o.j = uniform(so.j);
+  o.mt = __int_as_float(uniform(__float_as_int(so.mt)));
+  o.md = __int_as_float(uniform(__float_as_int(so.md)));
+  o.lnrho = __int_as_float(uniform(__float_as_int(so.lnrho)));
+  o.u = __int_as_float(uniform(__float_as_int(so.u)));
+  if (f < P.nF) item_wavefront<E>(P, e2, b, f, o, lane);
 }
 
 template <typename E>
@@ -1367,7 +1380,7 @@ int check_args(const void* t, const void* d, const int32_t* tok, const float* u,
 template <typename E>
 int launch(Params& P, hipStream_t stream) {
   const long long rows = (long long)(P.D + 1) * P.B * 2 * P.nchunk;
-  const long long items = ((long long)P.B * P.nF + kWaves - 1) / kWaves;
+  const long long items = (long long)P.B * ((P.nF + kWaves - 1) / kWaves);
   const long long picks = ((long long)P.B + kWaves - 1) / kWaves;
   if (rows > 0x7fffffffll || items > 0x7fffffffll) return SV_EINVAL;
 
