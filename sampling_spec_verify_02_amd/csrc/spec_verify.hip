@@ -294,22 +294,50 @@ __device__ inline void am_combine(float& v, int& i, float v2, int i2) {
   if (i < 0 || v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
 
-__device__ inline void wave_ms(float& m, float& s, float k) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float m2 = __shfl_xor(m, off);
-    const float s2 = __shfl_xor(s, off);
-    ms_combine(m, s, m2, s2, k);
-  }
+// Reduction of a float over the wavefront with DPP row shifts and row broadcasts (the steps of
+// dpp_scan below), the total read from lane 63 into every lane. Needs every lane active.
+template <int CTRL, int ROWS>
+__device__ inline float dpp_float(float x, float id) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(id), __float_as_int(x), CTRL,
+                                                    ROWS, 0xf, false));
+}
+template <typename Op>
+__device__ inline float dpp_total(float x, float id, Op op) {
+  x = op(x, dpp_float<0x111, 0xf>(x, id));   // row_shr:1
+  x = op(x, dpp_float<0x112, 0xf>(x, id));   // row_shr:2
+  x = op(x, dpp_float<0x114, 0xf>(x, id));   // row_shr:4
+  x = op(x, dpp_float<0x118, 0xf>(x, id));   // row_shr:8
+  x = op(x, dpp_float<0x142, 0xa>(x, id));   // row_bcast:15
+  x = op(x, dpp_float<0x143, 0xc>(x, id));   // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
+// (max, sum exp2((x - max) k)) over the wavefront: the max first, then each lane's sum rescaled
+// to it and added up (one exp2 per lane). Every lane gets the result.
+__device__ inline void wave_ms(float& m, float& s, float k) {
+  const float mw = dpp_total(m, -INFINITY, [](float a, float b) { return fmaxf(a, b); });
+  const float sr = (s == 0.f) ? 0.f : s * __builtin_amdgcn_exp2f((m - mw) * k);
+  s = dpp_total(sr, 0.f, [](float a, float b) { return a + b; });
+  m = mw;
+}
+
+// Argmax over the wavefront with the DPP steps of dpp_total (am_combine is associative and
+// commutative); every lane gets lane 63's result. Needs every lane active.
+template <int CTRL, int ROWS>
+__device__ inline void am_step(float& v, int& i) {
+  const float v2 = dpp_float<CTRL, ROWS>(v, -INFINITY);
+  const int i2 = __builtin_amdgcn_update_dpp(-1, i, CTRL, ROWS, 0xf, false);
+  am_combine(v, i, v2, i2);
+}
 __device__ inline void wave_am(float& v, int& i) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float v2 = __shfl_xor(v, off);
-    const int i2 = __shfl_xor(i, off);
-    am_combine(v, i, v2, i2);
-  }
+  am_step<0x111, 0xf>(v, i);
+  am_step<0x112, 0xf>(v, i);
+  am_step<0x114, 0xf>(v, i);
+  am_step<0x118, 0xf>(v, i);
+  am_step<0x142, 0xa>(v, i);
+  am_step<0x143, 0xc>(v, i);
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
 }
 
 // Natural log and exp from the hardware base-2 instructions (relative error near 1e-7; the
