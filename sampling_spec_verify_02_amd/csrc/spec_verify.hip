@@ -1044,14 +1044,19 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
       const int a = a0 + kFinBlock * k + kFinPer * lane;
       const int n = max(0, min(kFinPer, P.V - a));
       double ls = 0.0, wts[kFinPer];
+      if (n == kFinPer) {              // full run: no per-element branches, eight independent chains
+#pragma unroll
+        for (int e = 0; e < kFinPer; ++e)
+          wts[e] = exact_weight<E>(tr.r[k], dr.r[k], e, w, target_only, it, id);
+      } else {
+#pragma unroll
+        for (int e = 0; e < kFinPer; ++e)
+          wts[e] = e < n ? exact_weight<E>(tr.r[k], dr.r[k], e, w, target_only, it, id) : 0.0;
+      }
 #pragma unroll
       for (int e = 0; e < kFinPer; ++e) {
-        wts[e] = 0.0;
-        if (e < n) {
-          wts[e] = exact_weight<E>(tr.r[k], dr.r[k], e, w, target_only, it, id);
-          ls += wts[e];
-          if (wts[e] > 0.0) last_pos = a + e;
-        }
+        ls += wts[e];
+        if (wts[e] > 0.0) last_pos = a + e;
       }
       const double inc = dpp_scan_add(ls) + run;
       // lane l owns [prefix before l, prefix through l): consecutive stored values, one owner
