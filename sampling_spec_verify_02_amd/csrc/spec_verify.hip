@@ -106,13 +106,16 @@ struct Params {
   RowPart* rpart;     // [B][R][nchunk]
   FinPart* fpart;     // [B][nF]
   double* fmass;      // [B][nF] scratch of the pick
+  unsigned* done;     // [B] item workgroups finished (when the last one picks)
+  int merged;         // 1: the last item workgroup of a sequence does its pick
   float* dbg_row_stats;  // optional [B][R][2]
   int32_t* dbg_argmax;   // optional [B][D+1]
   float* dbg_logpq;      // optional [B][D][2]
 };
 
 // ------------------------------------------------------------------------------------------
-// device-coherent accesses (the pick's scratch masses: one lane stores, others load them back)
+// device-coherent accesses (item records that a pick in the same kernel may read; the pick's
+// scratch masses: one lane stores, others load them back)
 
 template <typename T>
 __device__ inline void st_dev(T* p, T v) {
@@ -121,6 +124,17 @@ __device__ inline void st_dev(T* p, T v) {
 template <typename T>
 __device__ inline T ld_dev(const T* p) {
   return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A load that is device-coherent when COH (data another workgroup of the same kernel stored with
+// st_dev), a plain one otherwise (data of an earlier kernel).
+template <bool COH, typename T>
+__device__ inline T ld_rec(const T* p) {
+  if constexpr (COH) return ld_dev(p);
+  else return *p;
+}
+
+__device__ inline unsigned add_dev(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Wait until this wavefront's earlier vector-memory operations (the stores of the scratch
 // masses) have completed, before they are loaded back.
@@ -890,17 +904,20 @@ __device__ inline double item_exact_mass(const Params& P, const E* trow, const E
 // the item records are read once, one per lane (r); beyond, they are re-read per pass.
 // The item records of sequence b that one pass of 64 lanes holds (all of them up to 64 items):
 // lane l gets item l's.
+template <bool COH>
 __device__ inline FinPart first_records(const Params& P, int b, int lane) {
   FinPart r = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, INFINITY, -INFINITY};
   if (P.nF <= 64 && lane < P.nF) {
     const FinPart& q = P.fpart[size_t(b) * P.nF + lane];
-    r.st = q.st; r.sd = q.sd; r.at = q.at; r.ad = q.ad;
-    r.bt = q.bt; r.bd = q.bd; r.dmin = q.dmin; r.dmax = q.dmax;
+    r.st = ld_rec<COH>(&q.st); r.sd = ld_rec<COH>(&q.sd);
+    r.at = ld_rec<COH>(&q.at); r.ad = ld_rec<COH>(&q.ad);
+    r.bt = ld_rec<COH>(&q.bt); r.bd = ld_rec<COH>(&q.bd);
+    r.dmin = ld_rec<COH>(&q.dmin); r.dmax = ld_rec<COH>(&q.dmax);
   }
   return r;
 }
 
-template <typename E>
+template <typename E, bool COH>
 __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w, const FinPart& r,
                                           int lane) {
   const int nF = P.nF;
@@ -915,8 +932,10 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
     FinPart x = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, INFINITY, -INFINITY};
     if (f < nF) {
       const FinPart& q = fp[f];
-      x.st = q.st; x.sd = q.sd; x.at = q.at; x.ad = q.ad;
-      x.bt = q.bt; x.bd = q.bd; x.dmin = q.dmin; x.dmax = q.dmax;
+      x.st = ld_rec<COH>(&q.st); x.sd = ld_rec<COH>(&q.sd);
+      x.at = ld_rec<COH>(&q.at); x.ad = ld_rec<COH>(&q.ad);
+      x.bt = ld_rec<COH>(&q.bt); x.bd = ld_rec<COH>(&q.bd);
+      x.dmin = ld_rec<COH>(&q.dmin); x.dmax = ld_rec<COH>(&q.dmax);
     }
     return x;
   };
@@ -1022,13 +1041,13 @@ __device__ __forceinline__ void wave_pick(const Params& P, int b, const Draw& w,
   const FinPart* rf = fp + fstar;
   const bool bonus = !w.residual;
   const bool blockwise = !past_end && !slow && (bonus || (!target_only &&
-                         !(rf->dmin <= rf->dmax)));
+                         !(ld_rec<COH>(&rf->dmin) <= ld_rec<COH>(&rf->dmax))));
   int kfirst = 0, klast = KB - 1;
   if (blockwise) {
     double bm = 0.0;                   // lane k: mass of block k
     if (lane < KB) {
-      const double ka = rf->kat[lane];
-      bm = bonus ? ka : fmax(0.0, ka * it - rf->kad[lane] * id);
+      const double ka = ld_rec<COH>(&rf->kat[lane]);
+      bm = bonus ? ka : fmax(0.0, ka * it - ld_rec<COH>(&rf->kad[lane]) * id);
     }
     const double inc = dpp_scan_add(bm) + run;
     const unsigned long long over = __ballot(lane < KB && inc > t);
@@ -1215,7 +1234,7 @@ __device__ __forceinline__ void item_sums(const Params& P, int b, int f, const D
       dmax = dpp_scan(dmax, -INFINITY, mx);
     }
   }
-  if (lane == 63) {                    // plain stores: the pick kernel runs after this kernel
+  if (lane == 63) {
     double at = 0.0, ad = 0.0, et = 0.0;
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
@@ -1224,12 +1243,21 @@ __device__ __forceinline__ void item_sums(const Params& P, int b, int f, const D
     }
     if (!w.residual) et = at;          // bonus draw: the block sums are sums of e_t
     FinPart* q = P.fpart + size_t(b) * P.nF + f;
-    q->st = w.residual ? st : et; q->sd = sd; q->at = at; q->ad = ad;
-    q->bt = bt; q->bd = bd; q->dmin = dmin; q->dmax = dmax;
+    FinPart x;
+    x.st = w.residual ? st : et; x.sd = sd; x.at = at; x.ad = ad;
+    x.bt = bt; x.bd = bd; x.dmin = dmin; x.dmax = dmax;
 #pragma unroll
     for (int k = 0; k < kMaxItemBlocks; ++k) {
-      q->kat[k] = k < KB ? kat[k] : 0.0;
-      q->kad[k] = k < KB ? kad[k] : 0.0;
+      x.kat[k] = k < KB ? kat[k] : 0.0;
+      x.kad[k] = k < KB ? kad[k] : 0.0;
+    }
+    if (P.merged) {                    // a pick in this kernel reads it
+      const double* src = reinterpret_cast<const double*>(&x);
+      double* dst = reinterpret_cast<double*>(q);
+#pragma unroll
+      for (int i = 0; i < int(sizeof(FinPart) / sizeof(double)); ++i) st_dev(dst + i, src[i]);
+    } else {
+      *q = x;
     }
   }
 }
@@ -1260,6 +1288,7 @@ __device__ __forceinline__ void row_workgroup(const Params& P, Shared& sm, int r
   const int b = (local / nc) % P.B;
   const int c = local % nc;
   const int D = P.D;
+  if (P.merged && rid < P.B && tid == 0) P.done[rid] = 0u;   // the item kernel counts from zero
   const int L = P.lens ? P.lens[b] : D;
   const float T = P.temperature[b];
   if (!seq_valid(L, D, T)) return;    // invalid length or temperature: nothing is read
@@ -1287,7 +1316,7 @@ __device__ __forceinline__ void pick_wavefront(const Params& P, const double* e2
   const Outcome o = {unsigned(a & 3u), int((a >> 2) & 31u), __uint_as_float(unsigned(a >> 32)),
                      __uint_as_float(unsigned(c)), __uint_as_float(unsigned(c >> 32)),
                      P.uniforms[size_t(b) * (P.D + 1) + P.D]};
-  wave_pick<E>(P, b, make_draw(P, b, o, e2), r, lane);
+  wave_pick<E, false>(P, b, make_draw(P, b, o, e2), r, lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1330,6 +1359,16 @@ __global__ __launch_bounds__(kThreads) void item_kernel(Params P) {
   o.lnrho = __int_as_float(uniform(__float_as_int(so.lnrho)));
   o.u = __int_as_float(uniform(__float_as_int(so.u)));
   if (f < P.nF) item_wavefront<E>(P, e2, b, f, o, lane);
+  if (!P.merged || (o.mode != kResidual && o.mode != kBonus)) return;
+  // The workgroup that completes the sequence's last items picks its token: each wavefront's
+  // record stores complete, then one count per workgroup.
+  __shared__ unsigned last;
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) last = add_dev(P.done + b, 1u) == unsigned(per_seq - 1) ? 1u : 0u;
+  __syncthreads();
+  if (wave != 0 || last == 0u) return;
+  wave_pick<E, true>(P, b, make_draw(P, b, o, e2), first_records<true>(P, b, lane), lane);
 }
 
 template <typename E>
@@ -1340,7 +1379,7 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(Params P) {
   __syncthreads();
   const int b = int(blockIdx.x) * kWaves + uniform(tid >> 6);
   if (b >= P.B) return;
-  const FinPart r = first_records(P, b, lane);
+  const FinPart r = first_records<false>(P, b, lane);
   const unsigned long long a = uniform64(P.pub[b].a);
   const unsigned long long c = uniform64(P.pub[b].c);
   pick_wavefront<E>(P, e2, b, r, a, c, lane);
@@ -1356,12 +1395,13 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // sequence) outnumber the items of the whole batch.
 inline int item_elems(int elem_bytes) { return kRowChunkBytes / elem_bytes / kItemsPerChunk; }
 
-// Workspace: [outcome words B][row partials][final-draw partials][pick scratch]. Every part is
-// written before it is read within one call, so a workspace needs no initialisation. One
+// Workspace: [outcome words B][row partials][final-draw partials][pick scratch][item counters B].
+// Every part is written before it is read within one call (the row kernel zeroes the counters),
+// so a workspace needs no initialisation. One
 // layout serves both dtypes (nF and nchunk are those of the dtype with more).
 struct Layout {
   int nchunk, nF;
-  size_t off_pub, off_rpart, off_fpart, off_fmass, total;
+  size_t off_pub, off_rpart, off_fpart, off_fmass, off_done, total;
 };
 
 inline bool make_layout(int B, int D, int V, Layout& L) {
@@ -1375,6 +1415,7 @@ inline bool make_layout(int B, int D, int V, Layout& L) {
   L.off_rpart = o; o += align256(size_t(B) * R * L.nchunk * sizeof(RowPart));
   L.off_fpart = o; o += align256(size_t(B) * L.nF * sizeof(FinPart));
   L.off_fmass = o; o += align256(size_t(B) * L.nF * sizeof(double));
+  L.off_done = o;  o += align256(size_t(B) * sizeof(unsigned));
   L.total = o;
   return true;
 }
@@ -1410,12 +1451,35 @@ int check_args(const void* t, const void* d, const int32_t* tok, const float* u,
   return SV_OK;
 }
 
+// Item workgroups resident at once on the current device (0 if unknown).
+template <typename E>
+long long item_capacity() {
+  static std::mutex m;
+  static std::map<int, long long> cap;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> g(m);
+  auto it = cap.find(dev);
+  if (it != cap.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  long long c = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, item_kernel<E>, kThreads, 0) ==
+          hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+    c = (long long)per_cu * cus;
+  cap[dev] = c;
+  return c;
+}
+
 template <typename E>
 int launch(Params& P, hipStream_t stream) {
   const long long rows = (long long)(P.D + 1) * P.B * 2 * P.nchunk;
   const long long items = (long long)P.B * ((P.nF + kWaves - 1) / kWaves);
   const long long picks = ((long long)P.B + kWaves - 1) / kWaves;
   if (rows > 0x7fffffffll || items > 0x7fffffffll) return SV_EINVAL;
+  // When every item workgroup is resident at once, the last one of each sequence picks its
+  // token (no pick kernel); otherwise a count would hold slots that later items need.
+  P.merged = items <= item_capacity<E>() ? 1 : 0;
 
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   {
@@ -1432,8 +1496,10 @@ int launch(Params& P, hipStream_t stream) {
   if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return SV_EHIP;
   hipLaunchKernelGGL(item_kernel<E>, dim3(unsigned(items)), dim3(kThreads), 0, stream, P);
   if (hipGetLastError() != hipSuccess) return SV_EHIP;
-  hipLaunchKernelGGL(pick_kernel<E>, dim3(unsigned(picks)), dim3(kThreads), 0, stream, P);
-  if (hipGetLastError() != hipSuccess) return SV_EHIP;
+  if (!P.merged) {
+    hipLaunchKernelGGL(pick_kernel<E>, dim3(unsigned(picks)), dim3(kThreads), 0, stream, P);
+    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+  }
   return SV_OK;
 }
 
@@ -1494,6 +1560,7 @@ int run(int dtype, const void* target, const void* draft, const int32_t* tokens,
   P.rpart = reinterpret_cast<RowPart*>(base + lay.off_rpart);
   P.fpart = reinterpret_cast<FinPart*>(base + lay.off_fpart);
   P.fmass = reinterpret_cast<double*>(base + lay.off_fmass);
+  P.done = reinterpret_cast<unsigned*>(base + lay.off_done);
   P.dbg_row_stats = dbg_stats;
   P.dbg_argmax = dbg_argmax;
   P.dbg_logpq = dbg_logpq;
