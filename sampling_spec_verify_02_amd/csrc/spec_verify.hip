@@ -27,8 +27,11 @@
 //   e_t / S_t - e_d / S_d, those clearly below contribute nothing, those inside the band are
 //   summed apart with the range of their x_t - x_d (one value means one exact ratio class,
 //   resolved exactly by the pick).
-// * Pick kernel: one wavefront per sequence. Exact normalisers from the item sums, the item
-//   masses, the item holding u * Z, and an fp64 prefix-scan rescan of that item give the token.
+// * Pick: one wavefront per sequence. Exact normalisers from the item sums, the item masses,
+//   the item and block holding u * Z, and an fp64 prefix-scan rescan of that block give the
+//   token. When every item workgroup of the call is resident at once, the item workgroup that
+//   completes a sequence's count picks (no third kernel); otherwise a pick kernel runs after
+//   the item kernel.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
