@@ -239,17 +239,6 @@ template <> struct Run<uint16_t> {
   __device__ float at(int e) const {
     return __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
   }
-  __device__ unsigned bits(int e) const {
-    return (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu);
-  }
-  // a copy whose values the compiler cannot equate with this one's (no common subexpressions
-  // kept alive across a long stretch of code)
-  __device__ Run opaque() const {
-    Run r = *this;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(r.w[k]));
-    return r;
-  }
 };
 template <> struct Run<float> {
   float x[kFinPer];
@@ -272,22 +261,10 @@ template <> struct Run<float> {
     x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
   }
   __device__ float at(int e) const { return x[e]; }
-  __device__ Run opaque() const {
-    Run r = *this;
-#pragma unroll
-    for (int e = 0; e < kFinPer; ++e) asm volatile("" : "+v"(r.x[e]));
-    return r;
-  }
 };
 
 // wave-uniform values kept in scalar registers
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ inline double uniform(double v) {
-  const unsigned long long u = __double_as_longlong(v);
-  const unsigned lo = __builtin_amdgcn_readfirstlane(unsigned(u));
-  const unsigned hi = __builtin_amdgcn_readfirstlane(unsigned(u >> 32));
-  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-}
 
 __device__ inline bool seq_valid(int L, int D, float T) {
   return L >= 0 && L <= D && isfinite(T) && T >= 0.f;
@@ -414,16 +391,6 @@ __device__ inline double lane_before(double x, double first) {
 __device__ inline double wave_sum(double x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-  return x;
-}
-__device__ inline double wave_min(double x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmin(x, __shfl_xor(x, off));
-  return x;
-}
-__device__ inline double wave_max(double x) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x = fmax(x, __shfl_xor(x, off));
   return x;
 }
 
