@@ -117,8 +117,8 @@ def main():
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (sequences shard over B with no "
-              "exchange; multi-GPU runs are not part of it). Use --gpus 1.", file=sys.stderr)
+        print("bench.py: runs on one GPU only (sequences would shard over B with no exchange; "
+              "a multi-GPU run is not implemented). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
