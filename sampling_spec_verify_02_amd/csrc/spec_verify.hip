@@ -100,6 +100,7 @@ struct Params {
   int32_t* out_len;
   int32_t* out_tokens;
   int B, D, V;
+  int b0, nb;         // the sequences [b0, b0 + nb) of this launch (grid y covers nb or 2 nb)
   int R;              // rows per sequence, 2D + 1 (target 0..D, then draft 0..D-1)
   int rch;            // elements per row chunk
   int nchunk;         // row chunks per row
@@ -1246,19 +1247,18 @@ __device__ inline bool draw_ready(unsigned long long a, unsigned long long c) {
 // ------------------------------------------------------------------------------------------
 // workgroups
 
+// Grid (nchunk, 2 nb, D+1), dispatched x fastest: position-major; within a position the target
+// rows of every sequence, then the draft rows (measured faster than alternating target and
+// draft rows per sequence); chunks of a row consecutive.
 template <typename E>
-__device__ __forceinline__ void row_workgroup(const Params& P, Shared& sm, int rid, int tid) {
-  const int nc = P.nchunk;
-  // position-major; within a position the target rows of every sequence, then the draft rows
-  // (measured faster than alternating target and draft rows per sequence)
-  const int per_p = P.B * 2 * nc;
-  const int p = rid / per_p;
-  const int local = rid - p * per_p;
-  const int which = local / (P.B * nc);               // 0 target row p, 1 draft row p
-  const int b = (local / nc) % P.B;
-  const int c = local % nc;
+__device__ __forceinline__ void row_workgroup(const Params& P, Shared& sm, int tid) {
+  const int c = int(blockIdx.x);
+  const int which = int(blockIdx.y) >= P.nb ? 1 : 0;  // 0 target row p, 1 draft row p
+  const int b = P.b0 + int(blockIdx.y) - which * P.nb;
+  const int p = int(blockIdx.z);
   const int D = P.D;
-  if (P.merged && rid < P.B && tid == 0) P.done[rid] = 0u;   // the item kernel counts from zero
+  if (P.merged && p == 0 && which == 0 && c == 0 && tid == 0)
+    P.done[b] = 0u;                                   // the item kernel counts from zero
   const int L = P.lens ? P.lens[b] : D;
   const float T = P.temperature[b];
   if (!seq_valid(L, D, T)) return;    // invalid length or temperature: nothing is read
@@ -1296,7 +1296,7 @@ __device__ __forceinline__ void pick_wavefront(const Params& P, const double* e2
 template <typename E>
 __global__ __launch_bounds__(kThreads) void row_kernel(Params P) {
   __shared__ Shared sm;
-  row_workgroup<E>(P, sm, int(blockIdx.x), threadIdx.x);
+  row_workgroup<E>(P, sm, threadIdx.x);
 }
 
 // Final-draw kernels, after the row kernel: outcome and partial sums (one wavefront per item),
@@ -1311,9 +1311,9 @@ __global__ __launch_bounds__(kThreads) void item_kernel(Params P) {
   __shared__ Outcome so;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const int per_seq = (P.nF + kWaves - 1) / kWaves;      // workgroups per sequence
-  const int b = int(blockIdx.x) / per_seq;
-  const int f = (int(blockIdx.x) - b * per_seq) * kWaves + wave;
+  const int per_seq = int(gridDim.x);                     // workgroups per sequence
+  const int b = P.b0 + int(blockIdx.y);
+  const int f = int(blockIdx.x) * kWaves + wave;
   if (wave == 0) {
     const OutcomeIn in = load_outcome(P, b, lane);
     const Outcome o = seq_outcome<E>(P, b, in, lane, f == 0);
@@ -1461,11 +1461,26 @@ int launch(Params& P, hipStream_t stream) {
     }
   }
   if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return SV_EHIP;
-  hipLaunchKernelGGL(row_kernel<E>, dim3(unsigned(rows)), dim3(kThreads), 0, stream, P);
-  if (hipGetLastError() != hipSuccess) return SV_EHIP;
+  // A grid's y dimension holds at most 65535 workgroups: larger batches launch in slices of
+  // sequences (stream-ordered, so each kernel still sees every earlier kernel's results).
+  constexpr int kRowSlice = 32767, kItemSlice = 65535;
+  for (int b0 = 0; b0 < P.B; b0 += kRowSlice) {
+    Params Q = P;
+    Q.b0 = b0;
+    Q.nb = std::min(kRowSlice, P.B - b0);
+    hipLaunchKernelGGL(row_kernel<E>, dim3(unsigned(Q.nchunk), unsigned(2 * Q.nb), unsigned(Q.D + 1)),
+                       dim3(kThreads), 0, stream, Q);
+    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+  }
   if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return SV_EHIP;
-  hipLaunchKernelGGL(item_kernel<E>, dim3(unsigned(items)), dim3(kThreads), 0, stream, P);
-  if (hipGetLastError() != hipSuccess) return SV_EHIP;
+  for (int b0 = 0; b0 < P.B; b0 += kItemSlice) {
+    Params Q = P;
+    Q.b0 = b0;
+    Q.nb = std::min(kItemSlice, P.B - b0);
+    hipLaunchKernelGGL(item_kernel<E>, dim3(unsigned((Q.nF + kWaves - 1) / kWaves), unsigned(Q.nb)),
+                       dim3(kThreads), 0, stream, Q);
+    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+  }
   if (!P.merged) {
     hipLaunchKernelGGL(pick_kernel<E>, dim3(unsigned(picks)), dim3(kThreads), 0, stream, P);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
