@@ -37,6 +37,8 @@ WORKLOADS = {
     "c3": "B=64 D=7 V=128256 bf16 T=1, Zipf(1.1)+N(0,1) target, draft +N(0,1)",
     "c4": "B=256 D=3 V=128256 bf16, half greedy / half T=0.7, 10% draft==target, else +N(0,1.5^2)",
     "c5": "B=512 D=7 V=129280 bf16 T=1, ragged L~U{1..7}, draft sigma_b~U[0.25,2]",
+    "mtp": "B=1024 D=1 V=129280 bf16 T=1, single-token verify, Zipf(1.1)+N(0,1) target, "
+           "draft +N(0,1)",
 }
 
 
@@ -58,14 +60,15 @@ def source_digest() -> str:
     return hashlib.sha256(open(SRC, "rb").read()).hexdigest()
 
 
-def read_traffic():
+def read_traffic(config: str, seed: int):
     """HBM bytes per launch of the row-statistics kernel from the committed rocprofv3 PMC
-    summary, or None if the kernel source changed since the counters were taken."""
+    summary, or None if the kernel source changed since the counters were taken or the
+    counters were taken on another workload."""
     try:
         t = json.load(open(TRAFFIC))
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != source_digest():
+    if t.get("source_sha256") != source_digest() or (config, seed) != ("c3", 0):
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -236,7 +239,7 @@ def main():
         "parity_unflagged_mismatches": mism,
         "roofline": {"bound": "hbm", "kernel": "row_kernel", "achieved": kern_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": kern_gbps / HBM_PEAK_GBPS,
-                     "traffic": read_traffic(), "kernel_ms": kern_ms},
+                     "traffic": read_traffic(args.config, args.seed), "kernel_ms": kern_ms},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

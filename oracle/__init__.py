@@ -1,5 +1,7 @@
-"""fp64 CPU oracle of the verification sampler. Test infrastructure only: used by tests/, the
-smoke check and the benchmark's CPU-baseline leg, never by the product path."""
+"""CPU oracles of the verification sampler (fp64) and of the epilogue that follows it. Test
+infrastructure only: used by tests/, the smoke check and the benchmark's CPU-baseline leg, never
+by the product path."""
 from .oracle import (Result, verify, verify_workload, tempered_log_softmax, softmax, accepts,
                      residual_weights, inverse_cdf, accept_window_measure, FLAG_TOL,
                      FINAL_WINDOW_MEASURE)
+from .advance import advance

@@ -8,7 +8,7 @@ from workloads import CONFIGS, make, bf16_round, bf16_decode
 from workloads.gen import _gumbel_argmax
 
 SMALL = dict(c1={}, c2=dict(V=3000), c3=dict(B=8, V=5000), c4=dict(B=40, V=5000),
-             c5=dict(B=32, V=5000))
+             c5=dict(B=32, V=5000), mtp=dict(B=64, V=5000))
 
 
 @pytest.mark.parametrize("cfg", sorted(CONFIGS))

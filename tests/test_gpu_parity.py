@@ -16,8 +16,8 @@ pytestmark = pytest.mark.gpu
 
 from tests import gpu_util as G  # noqa: E402
 
-# seeds per workload: 2000 / 1024 / 1024 / 2048 / 2048 rows
-SEEDS = dict(c1=2000, c2=64, c3=16, c4=8, c5=4)
+# seeds per workload: 2000 / 1024 / 1024 / 2048 / 2048 / 2048 rows
+SEEDS = dict(c1=2000, c2=64, c3=16, c4=8, c5=4, mtp=2)
 
 
 def _parity(cfg, seeds, **kw):
@@ -38,7 +38,7 @@ def _parity(cfg, seeds, **kw):
     return flagged, mism
 
 
-@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c3", "c4", "c5", "mtp"])
 def test_parity_full_size(cfg):
     _parity(cfg, SEEDS[cfg])
 

@@ -18,7 +18,7 @@ from oracle import verify, verify_workload
 from workloads import make
 
 SMALL = dict(c1={}, c2=dict(V=3000), c3=dict(B=12, V=4000), c4=dict(B=40, V=4000),
-             c5=dict(B=48, V=4000))
+             c5=dict(B=48, V=4000), mtp=dict(B=64, V=4000))
 
 
 @pytest.mark.parametrize("cfg", sorted(SMALL))

@@ -14,6 +14,8 @@ Workloads (the method's shapes: B sequences, D draft positions, vocabulary V):
                                   draft == target bit for bit; others draft = target + N(0, 1.5^2)
   c5  B=512 D=7  V=129280  bf16  T=1     ragged draft lengths L_b ~ U{1..7}, draft noise
                                   sigma_b ~ U[0.25, 2.0] per sequence, unused rows padded
+  mtp B=1024 D=1 V=129280  bf16  T=1     single-token (MTP-style) verification of a large decode
+                                  batch: Zipf target, draft = target + N(0, 1)
 
 Zipf target (c2..c5): logit(v) = -1.1 * ln(pi(v) + 1) - ln H_{V,1.1} + N(0, 1), where pi is one
 seeded permutation of the vocabulary per call (pi(v) = rank of token v) and
@@ -49,6 +51,7 @@ CONFIGS = {
     "c3": dict(cid=3, B=64, D=7, V=128256, dtype="bf16"),
     "c4": dict(cid=4, B=256, D=3, V=128256, dtype="bf16"),
     "c5": dict(cid=5, B=512, D=7, V=129280, dtype="bf16"),
+    "mtp": dict(cid=6, B=1024, D=1, V=129280, dtype="bf16"),
 }
 
 BF16_QNAN = np.uint16(0x7FC0)
