@@ -214,6 +214,23 @@ def main():
     kern_ms = float(np.mean(np.array(durs[:n.value], dtype=np.float64)))
     kern_gbps = alg_bytes / (kern_ms * 1e-3) / 1e9
 
+    # the epilogue (each sequence's window of its W = D+1 latest tokens moved by AL, lengths
+    # grown by AL) on the benched batch's outputs, timed alone with events on the same stream
+    W = w.D + 1
+    ids = torch.zeros((w.B, W), dtype=torch.int32, device=dev)
+    slen = torch.zeros(w.B, dtype=torch.int32, device=dev)
+    adv_args = (P(al), P(out), w.B, w.D, P(ids), W, P(slen), sp)
+    for _ in range(20):
+        if lib.spec_verify_advance(*adv_args) != 0:
+            raise RuntimeError("spec_verify_advance failed")
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(K):
+        lib.spec_verify_advance(*adv_args)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    adv_us = 1000.0 * e0.elapsed_time(e1) / K
+
     gbps = alg_bytes / (ms_step * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -241,6 +258,9 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": kern_gbps / HBM_PEAK_GBPS,
                      "traffic": read_traffic(args.config, args.seed), "kernel_ms": kern_ms},
         "cpu_baseline": None,
+        "advance": {"us_per_call": adv_us, "W": W,
+                    "note": "spec_verify_advance alone (not part of the step): window and "
+                            "lengths of the batch moved by AL on the GPU, no host sync"},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")

@@ -115,6 +115,27 @@ int spec_verify_debug(int dtype, const void* target_logits, const void* draft_lo
                       int32_t* out_tokens, float* row_stats, int32_t* row_argmax,
                       float* logpq_x, hipStream_t stream);
 
+/* Epilogue of a verification step, on the GPU with no host synchronisation ("Accélérer Sonar
+ * par la Spéculation", section "Calendrier MTP pour un jeton unique": the target's input tokens
+ * are shifted and a kernel writes the newly produced tokens into their slots; section
+ * "Inférence avec décodage spéculatif": the accepted count sets each sequence's next length).
+ *
+ *   accept_len [B]       int32, device: AL of each sequence (a spec_verify output).
+ *   tokens     [B][D+1]  int32, device: the emitted tokens (a spec_verify output).
+ *   input_ids  [B][W]    int32, device, updated in place: each sequence's W most recent
+ *                        tokens, oldest first. The window moves AL places towards the newest
+ *                        token and tokens[b][0..AL-1] fill its last AL slots (only the last W
+ *                        of them when AL > W). Must not overlap accept_len, tokens or seq_len.
+ *   seq_len    [B]       int32, device, updated in place: grows by AL. May be NULL.
+ *
+ * A sequence with AL outside [1, D+1] (AL = 0 marks a row spec_verify found invalid), or with
+ * seq_len[b] < 0 or seq_len[b] + AL > 2^31 - 1, is left unchanged. Enqueued on `stream` (run
+ * it on the stream of the spec_verify call whose outputs it reads); nothing is allocated or
+ * synchronised. Returns SV_EINVAL for a NULL required pointer, B <= 0, D outside [0, SV_MAX_D]
+ * or W <= 0 (enqueueing nothing), SV_ENODEV without a device, SV_EHIP for a failed launch. */
+int spec_verify_advance(const int32_t* accept_len, const int32_t* tokens, int B, int D,
+                        int32_t* input_ids, int W, int32_t* seq_len, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* spec_verify_strerror(int code);
 

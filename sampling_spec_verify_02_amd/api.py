@@ -113,3 +113,26 @@ def spec_verify_debug(target_logits, draft_logits, draft_tokens, draft_lens, uni
 
 def workspace_bytes(B: int, D: int, V: int) -> int:
     return int(lib().spec_verify_workspace_bytes(B, D, V))
+
+
+def spec_verify_advance(accept_len, tokens, input_ids, seq_len=None):
+    """Epilogue of a verification step, on the GPU: each sequence's window of recent tokens
+    input_ids [B][W] int32 moves by its AL and takes the emitted tokens at its end; seq_len [B]
+    int32 (optional) grows by AL. accept_len [B] and tokens [B][D+1] are spec_verify's outputs.
+    Updates input_ids and seq_len in place on torch's current stream; nothing is synchronised."""
+    if tokens.dim() != 2 or input_ids.dim() != 2:
+        raise ValueError("tokens must be [B][D+1] and input_ids [B][W]")
+    B, D1 = tokens.shape
+    dev = tokens.device
+    if dev.type != "cuda":
+        raise ValueError("tokens must be a GPU tensor")
+    _check(accept_len, "accept_len", torch.int32, (B,), dev)
+    _check(tokens, "tokens", torch.int32, (B, D1), dev)
+    _check(input_ids, "input_ids", torch.int32, (B, input_ids.shape[1]), dev)
+    if seq_len is not None:
+        _check(seq_len, "seq_len", torch.int32, (B,), dev)
+    rc = lib().spec_verify_advance(_ptr(accept_len), _ptr(tokens), B, D1 - 1, _ptr(input_ids),
+                                   int(input_ids.shape[1]), _ptr(seq_len), _stream(dev))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_advance")
+    return input_ids, seq_len

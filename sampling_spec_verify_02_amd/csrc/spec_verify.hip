@@ -1558,6 +1558,51 @@ int run(int dtype, const void* target, const void* draft, const int32_t* tokens,
   return dtype == 1 ? launch<uint16_t>(P, stream) : launch<float>(P, stream);
 }
 
+// Epilogue after verification ("Accélérer Sonar par la Spéculation", section "Calendrier MTP
+// pour un jeton unique": the input tokens are shifted and a kernel writes the new tokens into
+// their slots, with no host synchronisation). One wavefront per sequence: its window of the W
+// most recent tokens moves AL places and the AL emitted tokens fill the last slots; the length
+// grows by AL. The window is updated in place, 64 slots per pass in ascending order: slot j
+// takes slot j + AL (always a later slot) or an emitted token, and every lane's loads of a pass
+// complete before that pass's stores (the stored values are the loaded ones), so no slot is
+// overwritten before it has been read.
+__global__ void __launch_bounds__(kThreads) advance_kernel(const int32_t* __restrict__ accept_len,
+                                                           const int32_t* __restrict__ tokens,
+                                                           int B, int D, int32_t* input_ids,
+                                                           int W, int32_t* seq_len) {
+  const int lane = int(threadIdx.x) & 63;
+  const int b = int(blockIdx.x) * kWaves + int(threadIdx.x >> 6);
+  if (b >= B) return;
+  const int a = accept_len[b];
+  const int n = seq_len ? seq_len[b] : 0;
+  if (a < 1 || a > D + 1) return;
+  if (seq_len && (n < 0 || n > 0x7fffffff - a)) return;
+  int32_t* row = input_ids + size_t(b) * size_t(W);
+  const int32_t* emitted = tokens + size_t(b) * size_t(D + 1);
+  for (int j0 = 0; j0 < W; j0 += 64) {
+    const int j = j0 + lane;
+    if (j < W) {
+      const int src = j + a;
+      const int v = src < W ? row[src] : emitted[src - W];
+      row[j] = v;
+    }
+  }
+  if (seq_len && lane == 0) seq_len[b] = n + a;
+}
+
+int advance(const int32_t* accept_len, const int32_t* tokens, int B, int D, int32_t* input_ids,
+            int W, int32_t* seq_len, hipStream_t stream) {
+  if (B <= 0 || D < 0 || D > SV_MAX_D || W <= 0) return SV_EINVAL;
+  if (!accept_len || !tokens || !input_ids) return SV_EINVAL;
+  if ((unsigned long long)B * (unsigned long long)W > (1ull << 60)) return SV_EINVAL;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return SV_ENODEV;
+  const unsigned groups = unsigned((B + kWaves - 1) / kWaves);
+  hipLaunchKernelGGL(advance_kernel, dim3(groups), dim3(kThreads), 0, stream, accept_len, tokens,
+                     B, D, input_ids, W, seq_len);
+  return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
 }  // namespace sv
 
 extern "C" {
@@ -1603,6 +1648,11 @@ int spec_verify_debug(int dtype, const void* target_logits, const void* draft_lo
                  logpq_x, stream);
 }
 
+int spec_verify_advance(const int32_t* accept_len, const int32_t* tokens, int B, int D,
+                        int32_t* input_ids, int W, int32_t* seq_len, hipStream_t stream) {
+  return sv::advance(accept_len, tokens, B, D, input_ids, W, seq_len, stream);
+}
+
 const char* spec_verify_strerror(int code) {
   switch (code) {
     case SV_OK: return "ok";
@@ -1615,7 +1665,7 @@ const char* spec_verify_strerror(int code) {
   }
 }
 
-int spec_verify_version(void) { return 300; }
+int spec_verify_version(void) { return 301; }
 
 int spec_verify_profile_start(int max_calls) {
   if (max_calls <= 0 || max_calls > (1 << 20)) return SV_EINVAL;

@@ -23,7 +23,8 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for must in ("spec_verify_bf16", "spec_verify_f32", "spec_verify_ws",
-                 "spec_verify_workspace_bytes", "spec_verify_debug", "spec_verify_strerror"):
+                 "spec_verify_workspace_bytes", "spec_verify_debug", "spec_verify_strerror",
+                 "spec_verify_advance"):
         assert must in names
 
 
@@ -98,3 +99,20 @@ def test_no_device_is_reported():
         pytest.skip("a device is present: this host-only case would launch")
     assert _call("spec_verify_bf16") == _lib.SV_ENODEV
     assert _call("spec_verify_f32") == _lib.SV_ENODEV
+
+
+def test_advance_bad_arguments():
+    lib = _lib.lib()
+    E = _lib.SV_EINVAL
+    ok = dict(al=FAKE, tok=FAKE, B=4, D=3, ids=FAKE, W=8, lens=NUL)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.spec_verify_advance(a["al"], a["tok"], a["B"], a["D"], a["ids"], a["W"],
+                                       a["lens"], NUL)
+    assert call(B=0) == E and call(B=-1) == E
+    assert call(D=-1) == E and call(D=_lib.SV_MAX_D + 1) == E
+    assert call(W=0) == E and call(W=-5) == E
+    assert call(al=NUL) == E and call(tok=NUL) == E and call(ids=NUL) == E
+    if torch.cuda.device_count() == 0:
+        assert call() == _lib.SV_ENODEV
