@@ -32,6 +32,9 @@
 //   token. When every item workgroup of the call is resident at once, the item workgroup that
 //   completes a sequence's count picks (no third kernel); otherwise a pick kernel runs after
 //   the item kernel.
+// * Outcome kernel: only when the item grid takes more than one round of resident workgroups
+//   (large batches). One wavefront per sequence derives the outcome once, between the row and
+//   item kernels, and the item workgroups read it with one load instead of deriving it each.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -112,6 +115,8 @@ struct Params {
   double* fmass;      // [B][nF] scratch of the pick
   unsigned* done;     // [B] item workgroups finished (when the last one picks)
   int merged;         // 1: the last item workgroup of a sequence does its pick
+  int pre;            // 1: the outcome kernel has stored every outcome (item grids of more
+                      //    than one round); item workgroups read it instead of deriving it
   float* dbg_row_stats;  // optional [B][R][2]
   int32_t* dbg_argmax;   // optional [B][D+1]
   float* dbg_logpq;      // optional [B][D][2]
@@ -1315,9 +1320,18 @@ __global__ __launch_bounds__(kThreads) void item_kernel(Params P) {
   const int b = P.b0 + int(blockIdx.y);
   const int f = int(blockIdx.x) * kWaves + wave;
   if (wave == 0) {
-    const OutcomeIn in = load_outcome(P, b, lane);
-    const Outcome o = seq_outcome<E>(P, b, in, lane, f == 0);
-    if (lane == 0) so = o;
+    if (P.pre) {                       // stored by the outcome kernel
+      const unsigned long long a = uniform64(P.pub[b].a);
+      const unsigned long long c = uniform64(P.pub[b].c);
+      if (lane == 0)
+        so = Outcome{unsigned(a & 3u), int((a >> 2) & 31u), __uint_as_float(unsigned(a >> 32)),
+                     __uint_as_float(unsigned(c)), __uint_as_float(unsigned(c >> 32)),
+                     P.uniforms[size_t(b) * (P.D + 1) + P.D]};
+    } else {
+      const OutcomeIn in = load_outcome(P, b, lane);
+      const Outcome o = seq_outcome<E>(P, b, in, lane, f == 0);
+      if (lane == 0) so = o;
+    }
   }
   fill_e2(e2, tid);
   __syncthreads();
@@ -1339,6 +1353,19 @@ __global__ __launch_bounds__(kThreads) void item_kernel(Params P) {
   __syncthreads();
   if (wave != 0 || last == 0u) return;
   wave_pick<E, true>(P, b, make_draw(P, b, o, e2), first_records<true>(P, b, lane), lane);
+}
+
+// Outcome kernel (item grids of more than one round only): one wavefront per sequence derives
+// the outcome once and stores AL, the tokens other than the final draw's and the outcome words,
+// so that each of the sequence's item workgroups starts from one load rather than from the row
+// partials.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void outcome_kernel(Params P) {
+  const int lane = threadIdx.x & 63;
+  const int b = int(blockIdx.x) * kWaves + uniform(int(threadIdx.x >> 6));
+  if (b >= P.B) return;
+  const OutcomeIn in = load_outcome(P, b, lane);
+  (void)seq_outcome<E>(P, b, in, lane, true);
 }
 
 template <typename E>
@@ -1450,6 +1477,9 @@ int launch(Params& P, hipStream_t stream) {
   // When every item workgroup is resident at once, the last one of each sequence picks its
   // token (no pick kernel); otherwise a count would hold slots that later items need.
   P.merged = items <= item_capacity<E>() ? 1 : 0;
+  // More than one round of item workgroups: derive each outcome once, in its own kernel (one
+  // round, one wavefront per sequence), rather than once per item workgroup.
+  P.pre = P.merged ? 0 : 1;
 
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   {
@@ -1473,6 +1503,10 @@ int launch(Params& P, hipStream_t stream) {
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
   }
   if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return SV_EHIP;
+  if (P.pre) {
+    hipLaunchKernelGGL(outcome_kernel<E>, dim3(unsigned(picks)), dim3(kThreads), 0, stream, P);
+    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+  }
   for (int b0 = 0; b0 < P.B; b0 += kItemSlice) {
     Params Q = P;
     Q.b0 = b0;
