@@ -5,3 +5,4 @@ from .oracle import (Result, verify, verify_workload, tempered_log_softmax, soft
                      residual_weights, inverse_cdf, accept_window_measure, FLAG_TOL,
                      FINAL_WINDOW_MEASURE)
 from .advance import advance
+from .threshold import verify_threshold, verify_threshold_workload
