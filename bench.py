@@ -46,13 +46,13 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def valid_row_bytes(w) -> int:
+def valid_row_bytes(w, threshold=False) -> int:
     """Algorithmic logit bytes: every row the method needs, once (target rows 0..L_b, draft rows
-    0..L_b-1, no draft rows for greedy sequences)."""
+    0..L_b-1, no draft rows for greedy sequences or for threshold acceptance)."""
     rows = 0
     for b in range(w.B):
         L = int(w.lens[b])
-        rows += (L + 1) + (0 if w.temperature[b] == 0 else L)
+        rows += (L + 1) + (0 if (w.temperature[b] == 0 or threshold) else L)
     return rows * w.V * w.elem_bytes, rows
 
 
@@ -73,16 +73,19 @@ def read_traffic(config: str, seed: int):
     return t.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, seconds: float):
-    from oracle import verify
+def cpu_baseline(w, seconds: float, tau=None):
+    from oracle import verify, verify_threshold
 
     tgt, drf = w.target_f32(), w.draft_f32()
     lens = w.lens if w.lens_given else None
 
     def run(k):
         t0 = time.perf_counter()
-        verify(tgt[:k], drf[:k], w.tokens[:k], None if lens is None else lens[:k],
-               w.uniforms[:k], w.temperature[:k])
+        lk = None if lens is None else lens[:k]
+        if tau is None:
+            verify(tgt[:k], drf[:k], w.tokens[:k], lk, w.uniforms[:k], w.temperature[:k])
+        else:
+            verify_threshold(tgt[:k], w.tokens[:k], lk, w.uniforms[:k], w.temperature[:k], tau)
         return time.perf_counter() - t0
 
     per = run(min(2, w.B)) / min(2, w.B)
@@ -115,6 +118,9 @@ def main():
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--threshold", type=float, default=None,
+                    help="time threshold acceptance with this tau instead of the standard rule "
+                         "(target rows only)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device-to-device copies of 256 MiB (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -142,7 +148,8 @@ def main():
         return
     log(f"bench: generating {args.config} seed {args.seed}")
     w = make(args.config, args.seed)
-    alg_bytes, rows = valid_row_bytes(w)
+    tau = args.threshold
+    alg_bytes, rows = valid_row_bytes(w, tau is not None)
 
     def logits(a):
         if w.dtype == "bf16":
@@ -151,7 +158,7 @@ def main():
 
     ncopy = max(1, args.copies)
     tgts = [logits(w.target) for _ in range(ncopy)]
-    drfs = [logits(w.draft) for _ in range(ncopy)]
+    drfs = [logits(w.draft) if tau is None else None for _ in range(ncopy)]
     tok = torch.from_numpy(w.tokens).to(dev)
     lens = torch.from_numpy(w.lens).to(dev) if w.lens_given else None
     uni = torch.from_numpy(w.uniforms).to(dev)
@@ -159,12 +166,17 @@ def main():
     al = torch.empty(w.B, dtype=torch.int32, device=dev)
     out = torch.empty((w.B, w.D + 1), dtype=torch.int32, device=dev)
     lib = sv.lib()
-    fn = lib.spec_verify_bf16 if w.dtype == "bf16" else lib.spec_verify_f32
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr() if t is not None else 0)  # noqa: E731
-    calls = [(P(tgts[c]), P(drfs[c]), P(tok), P(lens), P(uni), w.B, w.D, w.V, P(temp), P(al),
-              P(out), sp) for c in range(ncopy)]
+    if tau is None:
+        fn = lib.spec_verify_bf16 if w.dtype == "bf16" else lib.spec_verify_f32
+        calls = [(P(tgts[c]), P(drfs[c]), P(tok), P(lens), P(uni), w.B, w.D, w.V, P(temp),
+                  P(al), P(out), sp) for c in range(ncopy)]
+    else:
+        fn = lib.spec_verify_threshold
+        calls = [(1 if w.dtype == "bf16" else 0, P(tgts[c]), P(tok), P(lens), P(uni), w.B, w.D,
+                  w.V, P(temp), float(tau), P(al), P(out), sp) for c in range(ncopy)]
 
     def step(k):
         rc = fn(*calls[k % ncopy])
@@ -174,8 +186,8 @@ def main():
     # correctness of the benchmarked call against the oracle on this workload
     step(0)
     torch.cuda.synchronize()
-    from oracle import verify_workload
-    ref = verify_workload(w)
+    from oracle import verify_threshold_workload, verify_workload
+    ref = verify_workload(w) if tau is None else verify_threshold_workload(w, tau)
     g_al, g_tok = al.cpu().numpy(), out.cpu().numpy()
     ok = ~ref.flagged
     mism = int(np.sum(ok & ((g_al != ref.accept_len) | np.any(g_tok != ref.tokens, axis=1))))
@@ -246,7 +258,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": f"{args.config}: {WORKLOADS[args.config]}", "B": w.B, "D": w.D,
-                   "V": w.V, "seed": args.seed, "input_copies_rotated": ncopy},
+                   "V": w.V, "seed": args.seed, "input_copies_rotated": ncopy,
+                   "acceptance": "standard" if tau is None else f"threshold tau={tau}"},
         "hbm_gbps": gbps,
         "pct_of_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
         "logit_rows_per_s": rows / (ms_step * 1e-3),
@@ -264,7 +277,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, tau)
     print(json.dumps(res), flush=True)
 
 

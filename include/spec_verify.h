@@ -115,6 +115,26 @@ int spec_verify_debug(int dtype, const void* target_logits, const void* draft_lo
                       int32_t* out_tokens, float* row_stats, int32_t* row_argmax,
                       float* logpq_x, hipStream_t stream);
 
+/* Threshold (relaxed) acceptance ("Accélérer Sonar par la Spéculation", section "Décodage
+ * spéculatif": each prefix of the candidates is scored with a probability and the longest one
+ * above an acceptance threshold is kept; the target gives one more token, sampled from its
+ * logits at the first position not kept, section "Génération cible").
+ *
+ *   For each sampled sequence (T_b > 0) with p_i = softmax(target[b][i] / T_b): the prefix
+ *   x_0..x_p is kept while sum_{i<=p} log p_i(x_i) > ln tau (its target probability is above
+ *   tau); j = the first position whose prefix is not kept (L_b if all are). AL = j + 1; the
+ *   tokens are x_0..x_{j-1}, then a draw from p_j by the inverse CDF in ascending token id with
+ *   the uniform u[b][D] (as spec_verify's bonus draw). Draft logits are not used: no draft
+ *   pointer is taken and no draft row is read. Greedy sequences (T_b = 0) follow spec_verify's
+ *   argmax matching, which is this rule for any tau in [0, 1).
+ *   tau: host float >= 0 (0 keeps every prefix; tau >= 1 keeps none); NaN or infinite gives
+ *   SV_EINVAL. dtype: 0 = fp32, 1 = bf16. Every other argument, the layouts, the per-row error
+ *   marks and the library workspace are those of spec_verify_bf16 / spec_verify_f32. */
+int spec_verify_threshold(int dtype, const void* target_logits, const int32_t* draft_tokens,
+                          const int32_t* draft_lens, const float* uniforms, int B, int D, int V,
+                          const float* temperature, float tau, int32_t* out_accept_len,
+                          int32_t* out_tokens, hipStream_t stream);
+
 /* Epilogue of a verification step, on the GPU with no host synchronisation ("Accélérer Sonar
  * par la Spéculation", section "Calendrier MTP pour un jeton unique": the target's input tokens
  * are shifted and a kernel writes the newly produced tokens into their slots; section

@@ -40,7 +40,8 @@ def _prepare(target, draft, draft_tokens, draft_lens, uniforms, temperature,
     if target.dtype not in _DT:
         raise TypeError(f"logits dtype must be bfloat16 or float32, got {target.dtype}")
     _check(target, "target_logits", target.dtype, (B, D + 1, V), dev)
-    _check(draft, "draft_logits", target.dtype, (B, D, V), dev)
+    if draft is not None:              # None only for threshold acceptance (no draft logits)
+        _check(draft, "draft_logits", target.dtype, (B, D, V), dev)
     _check(draft_tokens, "draft_tokens", torch.int32, (B, D), dev)
     if draft_lens is not None:
         _check(draft_lens, "draft_lens", torch.int32, (B,), dev)
@@ -87,6 +88,24 @@ def spec_verify(target_logits, draft_logits, draft_tokens, draft_lens, uniforms,
         rc = L.spec_verify_f32(*args, st)
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify")
+    return out_accept_len, out_tokens
+
+
+def spec_verify_threshold(target_logits, draft_tokens, draft_lens, uniforms, temperature, tau,
+                          out_accept_len=None, out_tokens=None):
+    """Threshold acceptance on the GPU: keep the longest draft prefix whose target probability is
+    above tau, then draw one more token from the target at the first position not kept. No draft
+    logits are taken. Returns (accept_len [B] int32, tokens [B][D+1] int32); enqueued on torch's
+    current stream, nothing is synchronised."""
+    B, D, V, temperature, out_accept_len, out_tokens = _prepare(
+        target_logits, None, draft_tokens, draft_lens, uniforms, temperature,
+        out_accept_len, out_tokens)
+    rc = lib().spec_verify_threshold(_DT[target_logits.dtype], _ptr(target_logits),
+                                     _ptr(draft_tokens), _ptr(draft_lens), _ptr(uniforms), B, D,
+                                     V, _ptr(temperature), float(tau), _ptr(out_accept_len),
+                                     _ptr(out_tokens), _stream(target_logits.device))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_threshold")
     return out_accept_len, out_tokens
 
 

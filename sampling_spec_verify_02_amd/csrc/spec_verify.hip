@@ -117,6 +117,8 @@ struct Params {
   int merged;         // 1: the last item workgroup of a sequence does its pick
   int pre;            // 1: the outcome kernel has stored every outcome (item grids of more
                       //    than one round); item workgroups read it instead of deriving it
+  int thresh;         // 1: threshold acceptance (prefix probability above tau; no draft rows)
+  double log_tau;     // ln tau of threshold acceptance (-inf for tau = 0)
   float* dbg_row_stats;  // optional [B][R][2]
   int32_t* dbg_argmax;   // optional [B][D+1]
   float* dbg_logpq;      // optional [B][D][2]
@@ -631,7 +633,7 @@ __device__ __forceinline__ Outcome seq_outcome(const Params& P, int b, const Out
   const float iT = 1.f / T;
   const float k2 = kLog2e * iT;
   const int pr = r <= D ? r : r - (D + 1);
-  const bool need = r < R && (r <= D ? pr <= L : (!greedy && pr < L));
+  const bool need = r < R && (r <= D ? pr <= L : (!greedy && !P.thresh && pr < L));
   float m = -INFINITY, s = 0.f, x = 0.f;
   int idx = -1;
   if (need) {
@@ -652,7 +654,7 @@ __device__ __forceinline__ Outcome seq_outcome(const Params& P, int b, const Out
   const int p = lane;
   bool rej = false;
   int g = -1;
-  float mt = 0.f, md = 0.f, lr = 0.f;
+  float mt = 0.f, md = 0.f, lr = 0.f, lpx = 0.f;
   if (p <= L) {
     if (greedy) {
       g = idx;
@@ -662,7 +664,13 @@ __device__ __forceinline__ Outcome seq_outcome(const Params& P, int b, const Out
       mt = m;
       const float lnt = ln_hw(s);
       float lnd = 0.f;
-      if (p < L) {
+      if (p < L && P.thresh) {
+        lpx = (x - mt) * iT - lnt;     // the test is taken below, on the running sum
+        if (write && P.dbg_logpq) {
+          P.dbg_logpq[(size_t(b) * D + p) * 2] = lpx;
+          P.dbg_logpq[(size_t(b) * D + p) * 2 + 1] = __int_as_float(0x7fc00000);
+        }
+      } else if (p < L) {
         md = md_l;
         lnd = ln_hw(sd_l);
         const float lp = (x - mt) * iT - lnt;
@@ -685,10 +693,18 @@ __device__ __forceinline__ Outcome seq_outcome(const Params& P, int b, const Out
       }
     }
   }
+  if (P.thresh && !greedy) {
+    // threshold acceptance ("Accélérer Sonar par la Spéculation", "Décodage spéculatif"): the
+    // prefix through position p is kept while sum_{i<=p} log p_i(x_i) > ln tau; the running sum
+    // in fp64 over the fp32 log-probabilities, lane p holding position p
+    const double cs = dpp_scan_add(p < L ? double(lpx) : 0.0);
+    rej = p < L && !(cs > P.log_tau);
+  }
   const unsigned long long rejm = __ballot(rej);
   const int j = rejm ? int(__builtin_ctzll(rejm)) : L;
   o.j = j;
-  o.mode = greedy ? kNoDraw : (j < L ? kResidual : kBonus);
+  // threshold acceptance draws the extra token from p_j at a rejection too (no residual)
+  o.mode = greedy ? kNoDraw : ((j < L && !P.thresh) ? kResidual : kBonus);
   o.mt = __shfl(mt, j);
   o.md = __shfl(md, j);
   o.lnrho = __shfl(lr, j);
@@ -1268,7 +1284,7 @@ __device__ __forceinline__ void row_workgroup(const Params& P, Shared& sm, int t
   const float T = P.temperature[b];
   if (!seq_valid(L, D, T)) return;    // invalid length or temperature: nothing is read
   const bool greedy = (T == 0.f);
-  if (which == 0 ? (p <= L) : (!greedy && p < L))      // rows the method needs
+  if (which == 0 ? (p <= L) : (!greedy && !P.thresh && p < L))   // rows the method needs
     row_chunk<E>(P, sm, b, p, which, c, L, T, greedy, tid);
 }
 
@@ -1439,10 +1455,10 @@ std::mutex g_prof_mutex;
 Profile g_prof;
 
 int check_args(const void* t, const void* d, const int32_t* tok, const float* u, const float* temp,
-               int32_t* ol, int32_t* ot, int B, int D, int V) {
+               int32_t* ol, int32_t* ot, int B, int D, int V, bool need_draft = true) {
   if (B <= 0 || D < 0 || V <= 0 || D > SV_MAX_D) return SV_EINVAL;
   if (!t || !u || !temp || !ol || !ot) return SV_EINVAL;
-  if (D > 0 && (!d || !tok)) return SV_EINVAL;
+  if (D > 0 && ((need_draft && !d) || !tok)) return SV_EINVAL;
   const unsigned __int128 n = (unsigned __int128)B * (unsigned __int128)(D + 1) * (unsigned __int128)V;
   if (n > ((unsigned __int128)1 << 60)) return SV_EINVAL;
   return SV_OK;
@@ -1525,9 +1541,11 @@ int launch(Params& P, hipStream_t stream) {
 int run(int dtype, const void* target, const void* draft, const int32_t* tokens,
         const int32_t* lens, const float* uniforms, int B, int D, int V, const float* temperature,
         int32_t* out_len, int32_t* out_tokens, void* ws, size_t ws_bytes, float* dbg_stats,
-        int32_t* dbg_argmax, float* dbg_logpq, hipStream_t stream) {
+        int32_t* dbg_argmax, float* dbg_logpq, hipStream_t stream, bool thresh = false,
+        double log_tau = 0.0) {
   if (dtype != 0 && dtype != 1) return SV_EDTYPE;
-  int rc = check_args(target, draft, tokens, uniforms, temperature, out_len, out_tokens, B, D, V);
+  int rc = check_args(target, draft, tokens, uniforms, temperature, out_len, out_tokens, B, D, V,
+                      !thresh);
   if (rc != SV_OK) return rc;
   Layout lay;
   make_layout(B, D, V, lay);
@@ -1580,6 +1598,8 @@ int run(int dtype, const void* target, const void* draft, const int32_t* tokens,
   P.fpart = reinterpret_cast<FinPart*>(base + lay.off_fpart);
   P.fmass = reinterpret_cast<double*>(base + lay.off_fmass);
   P.done = reinterpret_cast<unsigned*>(base + lay.off_done);
+  P.thresh = thresh ? 1 : 0;
+  P.log_tau = log_tau;
   P.dbg_row_stats = dbg_stats;
   P.dbg_argmax = dbg_argmax;
   P.dbg_logpq = dbg_logpq;
@@ -1680,6 +1700,17 @@ int spec_verify_debug(int dtype, const void* target_logits, const void* draft_lo
   return sv::run(dtype, target_logits, draft_logits, draft_tokens, draft_lens, uniforms, B, D,
                  V, temperature, out_accept_len, out_tokens, nullptr, 0, row_stats, row_argmax,
                  logpq_x, stream);
+}
+
+int spec_verify_threshold(int dtype, const void* target_logits, const int32_t* draft_tokens,
+                          const int32_t* draft_lens, const float* uniforms, int B, int D, int V,
+                          const float* temperature, float tau, int32_t* out_accept_len,
+                          int32_t* out_tokens, hipStream_t stream) {
+  if (!(tau >= 0.f) || std::isinf(tau)) return SV_EINVAL;
+  const double log_tau = tau > 0.f ? std::log(double(tau)) : -INFINITY;
+  return sv::run(dtype, target_logits, nullptr, draft_tokens, draft_lens, uniforms, B, D, V,
+                 temperature, out_accept_len, out_tokens, nullptr, 0, nullptr, nullptr, nullptr,
+                 stream, true, log_tau);
 }
 
 int spec_verify_advance(const int32_t* accept_len, const int32_t* tokens, int B, int D,

@@ -24,7 +24,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for must in ("spec_verify_bf16", "spec_verify_f32", "spec_verify_ws",
                  "spec_verify_workspace_bytes", "spec_verify_debug", "spec_verify_strerror",
-                 "spec_verify_advance"):
+                 "spec_verify_advance", "spec_verify_threshold"):
         assert must in names
 
 
@@ -115,4 +115,18 @@ def test_advance_bad_arguments():
     assert call(W=0) == E and call(W=-5) == E
     assert call(al=NUL) == E and call(tok=NUL) == E and call(ids=NUL) == E
     if torch.cuda.device_count() == 0:
+        assert call() == _lib.SV_ENODEV
+
+
+def test_threshold_bad_arguments():
+    lib = _lib.lib()
+    E = _lib.SV_EINVAL
+
+    def call(tau=0.01, dtype=1, t=FAKE, tok=FAKE, B=2, D=3, V=100):
+        return lib.spec_verify_threshold(dtype, t, tok, NUL, FAKE, B, D, V, FAKE, tau, FAKE,
+                                         FAKE, NUL)
+    assert call(tau=float("nan")) == E and call(tau=-0.5) == E and call(tau=float("inf")) == E
+    assert call(t=NUL) == E and call(tok=NUL) == E and call(B=0) == E and call(V=0) == E
+    assert call(dtype=5) == _lib.SV_EDTYPE
+    if torch.cuda.device_count() == 0:        # no draft pointer is needed
         assert call() == _lib.SV_ENODEV
