@@ -72,3 +72,19 @@ def test_verify_then_advance_on_one_stream(cfg, kw):
     assert ok.sum() > 0.9 * B
     assert np.array_equal(d_ids.cpu().numpy()[ok], ref_ids[ok])
     assert np.array_equal(d_lens.cpu().numpy()[ok], ref_lens[ok])
+
+
+def test_advance_large_batch():
+    """300,001 sequences (75,001 workgroups of four wavefronts)."""
+    rng = np.random.default_rng(8)
+    B, D, W = 300001, 3, 5
+    al = rng.integers(0, D + 2, B).astype(np.int32)
+    toks = rng.integers(0, 50000, (B, D + 1)).astype(np.int32)
+    ids = rng.integers(0, 50000, (B, W)).astype(np.int32)
+    lens = rng.integers(0, 100000, B).astype(np.int32)
+    ref_ids, ref_lens = advance(al, toks, D, ids, lens)
+    d_ids, d_lens = _dev(ids), _dev(lens)
+    sv.spec_verify_advance(_dev(al), _dev(toks), d_ids, d_lens)
+    torch.cuda.synchronize()
+    assert np.array_equal(d_ids.cpu().numpy(), ref_ids)
+    assert np.array_equal(d_lens.cpu().numpy(), ref_lens)

@@ -68,3 +68,22 @@ def test_threshold_never_reads_padding_or_drafts():
 def test_threshold_draft_lengths(D):
     w = make("c5", 13, B=40, V=3001, D=D)
     _check(w, 1e-4, f"D={D}")
+
+
+def test_threshold_batches_beyond_one_grid_slice():
+    """70,000 sequences: the row grid is launched in three slices of sequences and the item grid
+    in two; every slice must see its own sequences' partials."""
+    rng = np.random.default_rng(21)
+    B, D, V = 70000, 2, 40
+    tgt = (rng.standard_normal((B, D + 1, V)) * 1.5).astype(np.float32)
+    toks = rng.integers(0, V, (B, D)).astype(np.int32)
+    u = rng.random((B, D + 1), dtype=np.float32)
+    T = np.ones(B, np.float32)
+    from oracle import verify_threshold
+    ref = verify_threshold(tgt, toks, None, u, T, 0.05)
+    dev = G.device()
+    al, out = sv.spec_verify_threshold(torch.from_numpy(tgt).to(dev), torch.from_numpy(toks).to(dev),
+                                       None, torch.from_numpy(u).to(dev),
+                                       torch.from_numpy(T).to(dev), 0.05)
+    torch.cuda.synchronize()
+    G.compare(ref, al.cpu().numpy(), out.cpu().numpy(), "B=70000")
