@@ -163,8 +163,9 @@ const char* spec_verify_strerror(int code);
 int spec_verify_version(void);
 
 /* Timing hook for benchmarks. spec_verify_profile_start(n) creates n event pairs on the current
- * device; each following call (any entry point, up to n calls) records one pair around its
- * row-statistics kernel on the call's stream. spec_verify_profile_stop waits for those events,
+ * device; each following call (any entry point, up to n calls) times its row-statistics kernel
+ * on the call's stream with one pair: the kernel's own start and end stamps when it is one
+ * launch (B <= 32767), else event records around its launches. spec_verify_profile_stop waits for those events,
  * writes up to max_out durations in milliseconds to the host array out_ms (may be NULL), the
  * number of recorded calls to *n_recorded, and releases the events. Returns SV_EINVAL if not
  * started (stop) or already started (start), SV_EHIP on a runtime failure. */

@@ -35,6 +35,7 @@
 // * Outcome kernel: only when the item grid takes more than one round of resident workgroups
 //   (large batches). One wavefront per sequence derives the outcome once, between the row and
 //   item kernels, and the item workgroups read it with one load instead of deriving it each.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -1506,19 +1507,29 @@ int launch(Params& P, hipStream_t stream) {
       ++g_prof.used;
     }
   }
-  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return SV_EHIP;
   // A grid's y dimension holds at most 65535 workgroups: larger batches launch in slices of
   // sequences (stream-ordered, so each kernel still sees every earlier kernel's results).
   constexpr int kRowSlice = 32767, kItemSlice = 65535;
+  // Timing: a single row launch takes the events as its own start and end stamps; sliced
+  // launches are bracketed by event records.
+  const bool stamped = ev0 && P.B <= kRowSlice;
+  if (ev0 && !stamped && hipEventRecord(ev0, stream) != hipSuccess) return SV_EHIP;
   for (int b0 = 0; b0 < P.B; b0 += kRowSlice) {
     Params Q = P;
     Q.b0 = b0;
     Q.nb = std::min(kRowSlice, P.B - b0);
-    hipLaunchKernelGGL(row_kernel<E>, dim3(unsigned(Q.nchunk), unsigned(2 * Q.nb), unsigned(Q.D + 1)),
-                       dim3(kThreads), 0, stream, Q);
-    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    const dim3 grid(unsigned(Q.nchunk), unsigned(2 * Q.nb), unsigned(Q.D + 1));
+    if (stamped) {
+      void* args[] = {&Q};
+      if (hipExtLaunchKernel(reinterpret_cast<const void*>(&row_kernel<E>), grid, dim3(kThreads),
+                             args, 0, stream, ev0, ev1, 0) != hipSuccess)
+        return SV_EHIP;
+    } else {
+      hipLaunchKernelGGL(row_kernel<E>, grid, dim3(kThreads), 0, stream, Q);
+      if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    }
   }
-  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return SV_EHIP;
+  if (ev1 && !stamped && hipEventRecord(ev1, stream) != hipSuccess) return SV_EHIP;
   if (P.pre) {
     hipLaunchKernelGGL(outcome_kernel<E>, dim3(unsigned(picks)), dim3(kThreads), 0, stream, P);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
