@@ -130,3 +130,12 @@ def test_threshold_bad_arguments():
     assert call(dtype=5) == _lib.SV_EDTYPE
     if torch.cuda.device_count() == 0:        # no draft pointer is needed
         assert call() == _lib.SV_ENODEV
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """No CPU fallback: with the shared library absent the binding raises instead of computing
+    anything another way."""
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libspecverify.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.lib()
