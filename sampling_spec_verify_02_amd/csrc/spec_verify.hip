@@ -6,14 +6,19 @@
 // spéculatif"), in-order acceptance up to the first mismatch and AL in [1, 1 + D] from
 // "NVIDIA: öt irányelv ..." (section "Mit csinál a spekulatív dekódolás?").
 //
-// Three kernels per call, in stream order; each hands its results to the next through the
-// kernel boundary, so no kernel waits for another workgroup and none uses atomics.
+// Two to four kernels per call, in stream order: the row kernel, then (item grids of more than
+// one round of resident workgroups only) the outcome kernel, the item kernel, and (then too)
+// the pick kernel. Each hands its results to the next through the kernel boundary; no workgroup
+// waits for another. Inside the item kernel, when its grid is one round, the workgroups of a
+// sequence count their finished items (one atomic per workgroup) and the last one picks.
+// Threshold acceptance runs the same kernels without the draft rows; the epilogue that moves
+// each sequence's token window by AL is a kernel of its own, enqueued after verification.
 //
 // * Row kernel: one workgroup per 32 KB chunk of a row, position-major order (the position-0
-//   target rows of the batch, then its position-0 draft rows, then position 1, ...). It streams its chunk with non-temporal
-//   16-byte loads and stores the chunk's exact max and fp32 sum exp((x - max) / T) (sampled
-//   rows) or max and lowest argmax (greedy target rows); the chunk holding the draft token x_p
-//   also records the logit at x_p. Rows the method does not need (padding, draft rows of greedy
+//   target rows of the batch, then its position-0 draft rows, then position 1, ...). It streams
+//   its chunk with non-temporal 16-byte loads and stores the chunk's exact max and fp32
+//   sum exp((x - max) / T) (sampled rows) or max and lowest argmax (greedy target rows); the
+//   chunk holding the draft token x_p also records the logit at x_p. Rows the method does not need (padding, draft rows of greedy
 //   sequences, rows of invalid sequences) are not read.
 // * Item kernel: one wavefront per final-draw item (b, f). The wavefront first derives sequence
 //   b's outcome from the row partials: per-row statistics by a fixed combine tree, the test
