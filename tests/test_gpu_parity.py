@@ -261,3 +261,27 @@ def test_temperature_extremes(T):
     ref = verify_workload(w)
     al, toks = G.run(w)
     G.compare(ref, al, toks, f"T={T}")
+
+
+def test_concurrent_calls_on_two_streams():
+    """Two streams, each with its own library workspace, run interleaved calls on different
+    batches (one with the in-kernel pick, one with the outcome and pick kernels) without host
+    synchronisation between them; every result matches the oracle."""
+    import sampling_spec_verify_02_amd as sv
+    dev = G.device()
+    works = [make("c3", 60, B=32, V=30011), make("c5", 61, B=300)]
+    refs = [verify_workload(w) for w in works]
+    args = [G.to_dev(w, dev) for w in works]
+    streams = [torch.cuda.Stream(dev), torch.cuda.Stream(dev)]
+    outs = [[], []]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i in (0, 1):
+            with torch.cuda.stream(streams[i]):
+                a = args[i]
+                outs[i].append(sv.spec_verify(a["target"], a["draft"], a["tokens"], a["lens"],
+                                              a["uniforms"], a["temperature"]))
+    torch.cuda.synchronize()
+    for i in (0, 1):
+        for al, toks in outs[i]:
+            G.compare(refs[i], al.cpu().numpy(), toks.cpu().numpy(), f"stream {i}")
