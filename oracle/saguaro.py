@@ -13,9 +13,9 @@ Reading adopted: the draft is sampled from q' = normalise(q with its top-k token
 factor c, 0 < c <= 1); in logits, l' = l + T ln c on the row's top-k tokens (ties: lowest index)
 and l elsewhere, since softmax(l'/T) is then exactly q'. Verification must use the distribution
 the draft was actually sampled from, so the verifier runs unchanged on the reshaped draft
-logits, and stays lossless for any c. The arithmetic is fixed for bit-exact parity: ln c is
-rounded to fp32 on the host, delta = fp32(T * ln c), the new logit = fp32(l + delta), rounded to
-bf16 (nearest, ties to even) for bf16 storage. Greedy sequences (T = 0: delta = 0), rows at
+logits, and stays lossless for any c. The arithmetic is fixed for bit-exact parity: c is an fp32
+value (the boundary takes it as one), ln c is rounded to fp32, delta = fp32(T * ln c), the new
+logit = fp32(l + delta), rounded to bf16 (nearest, ties to even) for bf16 storage. Greedy sequences (T = 0: delta = 0), rows at
 positions >= L_b and sequences with an invalid length or temperature are left unchanged.
 """
 from __future__ import annotations
@@ -48,7 +48,7 @@ def reshape_draft(draft: np.ndarray, dtype: str, lens, temperature: np.ndarray, 
     B, D, V = draft.shape
     if lens is None:
         lens = np.full(B, D, np.int32)
-    lnf = np.float32(math.log(factor))
+    lnf = np.float32(math.log(float(np.float32(factor))))   # ln of the fp32 factor
     for b in range(B):
         L, T = int(lens[b]), float(temperature[b])
         if not (0 <= L <= D) or not (math.isfinite(T) and T > 0.0):
