@@ -135,6 +135,27 @@ int spec_verify_threshold(int dtype, const void* target_logits, const int32_t* d
                           const float* temperature, float tau, int32_t* out_accept_len,
                           int32_t* out_tokens, hipStream_t stream);
 
+/* Saguaro draft reshaping ("Speculative Speculative Decoding - асинхронизируй это", saguaro
+ * sampling: the draft's top-5 tokens get their probabilities lowered when the draft is
+ * generated, so that the residual the target samples after a rejection concentrates on them;
+ * the page gives no factor or formula). Reshapes draft logits in place so that softmax(l'/T) is
+ * q with its top-k tokens scaled by `factor` and renormalised: for every sampled sequence
+ * (T_b > 0) and position i < L_b, the k largest logits of draft row [b][i] (ties: lowest index)
+ * become fp32(l + fp32(T_b * ln factor)) (ln factor rounded to fp32 on the host; bf16 rows round
+ * the sum to nearest, ties to even). Draw the draft tokens from the reshaped rows and pass the
+ * same rows to spec_verify: verification against the distribution the drafts came from stays
+ * lossless for any factor.
+ *   dtype 0 = fp32, 1 = bf16; draft_logits [B][D][V] device, updated in place; draft_lens [B]
+ *   (NULL: all D) and temperature [B] device as for spec_verify. Greedy sequences, rows at
+ *   positions >= L_b and sequences with an invalid length or temperature are left unchanged.
+ *   factor in (0, 1]; k in [1, 8] (the page's choice is 5; k > V reshapes every token).
+ * Returns SV_EINVAL (factor or k out of range, bad sizes, NULL draft_logits with D > 0 or NULL
+ * temperature), SV_EDTYPE, SV_ENODEV or SV_EHIP, enqueueing nothing on an argument error. Logits
+ * must be finite in the rows it reads. Nothing is allocated or synchronised. */
+int spec_verify_saguaro_reshape(int dtype, void* draft_logits, const int32_t* draft_lens,
+                                const float* temperature, int B, int D, int V, float factor,
+                                int k, hipStream_t stream);
+
 /* Epilogue of a verification step, on the GPU with no host synchronisation ("Accélérer Sonar
  * par la Spéculation", section "Calendrier MTP pour un jeton unique": the target's input tokens
  * are shifted and a kernel writes the newly produced tokens into their slots; section

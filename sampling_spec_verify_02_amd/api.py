@@ -155,3 +155,28 @@ def spec_verify_advance(accept_len, tokens, input_ids, seq_len=None):
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_advance")
     return input_ids, seq_len
+
+
+def spec_verify_saguaro_reshape(draft_logits, draft_lens, temperature, factor, k=5):
+    """Saguaro reshaping of draft logits [B][D][V] (bfloat16 or float32, in place): the top-k
+    logits of every needed row move by T ln(factor), so that the row's softmax is q with its
+    top k scaled by `factor` and renormalised. draft_lens [B] int32 or None; temperature: [B]
+    float32 tensor or a Python float. Enqueued on torch's current stream."""
+    if draft_logits.dim() != 3:
+        raise ValueError("draft_logits must be [B][D][V]")
+    B, D, V = draft_logits.shape
+    dev = draft_logits.device
+    if draft_logits.dtype not in _DT:
+        raise TypeError(f"logits dtype must be bfloat16 or float32, got {draft_logits.dtype}")
+    _check(draft_logits, "draft_logits", draft_logits.dtype, (B, D, V), dev)
+    if draft_lens is not None:
+        _check(draft_lens, "draft_lens", torch.int32, (B,), dev)
+    if not torch.is_tensor(temperature):
+        temperature = torch.full((B,), float(temperature), dtype=torch.float32, device=dev)
+    _check(temperature, "temperature", torch.float32, (B,), dev)
+    rc = lib().spec_verify_saguaro_reshape(_DT[draft_logits.dtype], _ptr(draft_logits),
+                                           _ptr(draft_lens), _ptr(temperature), B, D, V,
+                                           float(factor), int(k), _stream(dev))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_saguaro_reshape")
+    return draft_logits

@@ -1660,6 +1660,116 @@ __global__ void __launch_bounds__(kThreads) advance_kernel(const int32_t* __rest
   if (seq_len && lane == 0) seq_len[b] = n + a;
 }
 
+// Saguaro draft reshaping ("Speculative Speculative Decoding - асинхронизируй это", saguaro
+// sampling: the draft's most likely tokens get their probabilities lowered when the draft is
+// generated). For each needed draft row (sampled sequence, position < L_b) the k largest logits
+// (ties: lowest index) move by delta = T ln c, which multiplies their probabilities under q by c
+// before renormalisation. One workgroup per row: every thread keeps the sorted top kMaxTopK of
+// its elements (strided by the workgroup), each wavefront then extracts its top k by k rounds of
+// a wavefront argmax, and wavefront 0 merges the four lists the same way; k lanes write the new
+// logits (fp32 sum without contraction, then bf16 round-to-nearest-even for bf16 rows).
+constexpr int kMaxTopK = 8;
+
+__device__ inline bool tk_better(float a, int ia, float b, int ib) {
+  return ib < 0 || a > b || (a == b && ia < ib);
+}
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void reshape_kernel(E* draft, const int32_t* lens,
+                                                           const float* temperature, int b0,
+                                                           int D, int V, float lnf, int k) {
+  const int i = int(blockIdx.x);
+  const int b = b0 + int(blockIdx.y);
+  const int tid = int(threadIdx.x), lane = tid & 63, wave = tid >> 6;
+  const int L = lens ? lens[b] : D;
+  const float T = temperature[b];
+  if (!seq_valid(L, D, T) || !(T > 0.f) || i >= L) return;     // the same for the workgroup
+  E* row = draft + (size_t(b) * D + i) * size_t(V);
+  float tv[kMaxTopK];
+  int ti[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) { tv[j] = -INFINITY; ti[j] = -1; }
+  for (int v = tid; v < V; v += kThreads) {
+    const float x = Elem<E>::get(row, size_t(v));
+    if (tk_better(x, v, tv[kMaxTopK - 1], ti[kMaxTopK - 1])) {
+      float cx = x;
+      int cv = v;
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        if (tk_better(cx, cv, tv[j], ti[j])) {
+          const float t = tv[j]; tv[j] = cx; cx = t;
+          const int u = ti[j]; ti[j] = cv; cv = u;
+        }
+      }
+    }
+  }
+  __shared__ float sval[kWaves][kMaxTopK];
+  __shared__ int sidx[kWaves][kMaxTopK];
+  for (int r = 0; r < k; ++r) {                    // the wavefront's top k, best first
+    float hv = tv[0];
+    int hi = ti[0];
+    wave_am(hv, hi);
+    if (hi >= 0 && ti[0] == hi) {                  // the owner drops its head
+#pragma unroll
+      for (int j = 0; j + 1 < kMaxTopK; ++j) { tv[j] = tv[j + 1]; ti[j] = ti[j + 1]; }
+      tv[kMaxTopK - 1] = -INFINITY;
+      ti[kMaxTopK - 1] = -1;
+    }
+    if (lane == 0) { sval[wave][r] = hv; sidx[wave][r] = hi; }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float cv = -INFINITY;
+  int ci = -1;
+  if (lane < kWaves * k) { cv = sval[lane / k][lane % k]; ci = sidx[lane / k][lane % k]; }
+  float myv = 0.f;
+  int mine = -1;
+  for (int r = 0; r < k; ++r) {                    // the row's top k
+    float hv = cv;
+    int hi = ci;
+    wave_am(hv, hi);
+    if (hi >= 0 && ci == hi) ci = -1;
+    if (lane == r) { myv = hv; mine = hi; }
+  }
+  if (lane < k && mine >= 0) {
+    const float sum = __fadd_rn(myv, __fmul_rn(T, lnf));
+    if constexpr (sizeof(E) == 2) {
+      const uint32_t u = __float_as_uint(sum);
+      row[mine] = E((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    } else {
+      row[mine] = E(sum);
+    }
+  }
+}
+
+int saguaro_reshape(int dtype, void* draft, const int32_t* lens, const float* temperature, int B,
+                    int D, int V, float factor, int k, hipStream_t stream) {
+  if (dtype != 0 && dtype != 1) return SV_EDTYPE;
+  if (B <= 0 || D < 0 || V <= 0 || D > SV_MAX_D || k < 1 || k > kMaxTopK) return SV_EINVAL;
+  if (!(factor > 0.f) || !(factor <= 1.f)) return SV_EINVAL;
+  if (!temperature || (D > 0 && !draft)) return SV_EINVAL;
+  if ((unsigned __int128)B * (unsigned __int128)(D + 1) * (unsigned __int128)V >
+      ((unsigned __int128)1 << 60))
+    return SV_EINVAL;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return SV_ENODEV;
+  if (D == 0) return SV_OK;
+  const float lnf = float(std::log(double(factor)));
+  const int kk = std::min(k, V);
+  constexpr int kSlice = 65535;
+  for (int b0 = 0; b0 < B; b0 += kSlice) {
+    const dim3 grid(unsigned(D), unsigned(std::min(kSlice, B - b0)));
+    if (dtype == 1)
+      hipLaunchKernelGGL(reshape_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
+                         static_cast<uint16_t*>(draft), lens, temperature, b0, D, V, lnf, kk);
+    else
+      hipLaunchKernelGGL(reshape_kernel<float>, grid, dim3(kThreads), 0, stream,
+                         static_cast<float*>(draft), lens, temperature, b0, D, V, lnf, kk);
+    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+  }
+  return SV_OK;
+}
+
 int advance(const int32_t* accept_len, const int32_t* tokens, int B, int D, int32_t* input_ids,
             int W, int32_t* seq_len, hipStream_t stream) {
   if (B <= 0 || D < 0 || D > SV_MAX_D || W <= 0) return SV_EINVAL;
@@ -1727,6 +1837,13 @@ int spec_verify_threshold(int dtype, const void* target_logits, const int32_t* d
   return sv::run(dtype, target_logits, nullptr, draft_tokens, draft_lens, uniforms, B, D, V,
                  temperature, out_accept_len, out_tokens, nullptr, 0, nullptr, nullptr, nullptr,
                  stream, true, log_tau);
+}
+
+int spec_verify_saguaro_reshape(int dtype, void* draft_logits, const int32_t* draft_lens,
+                                const float* temperature, int B, int D, int V, float factor,
+                                int k, hipStream_t stream) {
+  return sv::saguaro_reshape(dtype, draft_logits, draft_lens, temperature, B, D, V, factor, k,
+                             stream);
 }
 
 int spec_verify_advance(const int32_t* accept_len, const int32_t* tokens, int B, int D,

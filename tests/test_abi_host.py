@@ -24,7 +24,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for must in ("spec_verify_bf16", "spec_verify_f32", "spec_verify_ws",
                  "spec_verify_workspace_bytes", "spec_verify_debug", "spec_verify_strerror",
-                 "spec_verify_advance", "spec_verify_threshold"):
+                 "spec_verify_advance", "spec_verify_threshold", "spec_verify_saguaro_reshape"):
         assert must in names
 
 
@@ -139,3 +139,18 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(ImportError):
         _lib.lib()
+
+
+def test_saguaro_bad_arguments():
+    lib = _lib.lib()
+    E = _lib.SV_EINVAL
+
+    def call(dtype=1, d=FAKE, temp=FAKE, B=2, D=3, V=100, factor=0.5, k=5):
+        return lib.spec_verify_saguaro_reshape(dtype, d, NUL, temp, B, D, V, factor, k, NUL)
+    assert call(factor=0.0) == E and call(factor=1.5) == E and call(factor=float("nan")) == E
+    assert call(k=0) == E and call(k=9) == E
+    assert call(B=0) == E and call(V=0) == E and call(D=-1) == E and call(D=_lib.SV_MAX_D + 1) == E
+    assert call(d=NUL) == E and call(temp=NUL) == E
+    assert call(dtype=3) == _lib.SV_EDTYPE
+    if torch.cuda.device_count() == 0:
+        assert call() == _lib.SV_ENODEV

@@ -1,0 +1,66 @@
+"""GPU parity of Saguaro draft reshaping (spec_verify_saguaro_reshape through the C ABI) against
+the CPU oracle: the reshaped logits bit-exact for bf16 and fp32 rows, every k, vocabularies
+smaller than a workgroup and with ties, greedy, invalid and ragged sequences left alone; then
+reshaping followed by verification on the GPU against the oracle's reshaping and verification."""
+import numpy as np
+import pytest
+import torch
+
+import sampling_spec_verify_02_amd as sv
+from oracle import verify
+from oracle.saguaro import reshape_draft
+from workloads import make
+
+pytestmark = pytest.mark.gpu
+
+from tests import gpu_util as G  # noqa: E402
+
+
+def _reshape_on_gpu(w, factor, k):
+    d = G.logits_to_dev(w.draft, w.dtype, G.device())
+    lens = torch.from_numpy(w.lens).to(G.device()) if w.lens_given else None
+    sv.spec_verify_saguaro_reshape(d, lens, torch.from_numpy(w.temperature).to(G.device()),
+                                   factor, k)
+    torch.cuda.synchronize()
+    out = d.cpu()
+    return out.view(torch.int16).numpy().view(np.uint16) if w.dtype == "bf16" else out.numpy()
+
+
+@pytest.mark.parametrize("cfg,kw,factor,k", [
+    ("c3", dict(B=24), 0.5, 5), ("c3", dict(B=8, V=1000), 0.05, 8), ("c3", dict(B=8, V=7), 0.3, 5),
+    ("c2", dict(B=8), 0.5, 1), ("c2", dict(B=6, V=100), 0.9, 8), ("c4", dict(B=40), 0.25, 5),
+    ("c5", dict(B=48), 0.5, 5)])
+def test_reshape_matches_oracle(cfg, kw, factor, k):
+    w = make(cfg, 70, **kw)
+    if cfg == "c5":
+        w.lens[5] = w.D + 3            # invalid length: the sequence is left alone
+    got = _reshape_on_gpu(w, factor, k)
+    want = reshape_draft(w.draft, w.dtype, w.lens if w.lens_given else None, w.temperature,
+                         factor, k)
+    assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+
+
+def test_reshape_ties_take_lowest_indices():
+    rng = np.random.default_rng(3)
+    w = make("c2", 71, B=6, V=3000)
+    w.draft[:] = rng.integers(-2, 3, w.draft.shape).astype(np.float32)   # thousands of ties
+    got = _reshape_on_gpu(w, 0.5, 8)
+    want = reshape_draft(w.draft, "f32", None, w.temperature, 0.5, 8)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("cfg,kw", [("c3", dict(B=32, V=20011)), ("c5", dict(B=64, V=9001))])
+def test_reshape_then_verify(cfg, kw):
+    w = make(cfg, 72, **kw)
+    shaped = reshape_draft(w.draft, w.dtype, w.lens if w.lens_given else None, w.temperature,
+                           0.3, 5)
+    dec = (shaped.astype(np.uint32) << np.uint32(16)).view(np.float32) if w.dtype == "bf16" \
+        else shaped
+    ref = verify(w.target_f32(), dec, w.tokens, w.lens if w.lens_given else None, w.uniforms,
+                 w.temperature)
+    t = G.to_dev(w)
+    sv.spec_verify_saguaro_reshape(t["draft"], t["lens"], t["temperature"], 0.3, 5)
+    al, toks = sv.spec_verify(t["target"], t["draft"], t["tokens"], t["lens"], t["uniforms"],
+                              t["temperature"])
+    torch.cuda.synchronize()
+    G.compare(ref, al.cpu().numpy(), toks.cpu().numpy(), f"{cfg} reshaped")
