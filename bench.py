@@ -243,6 +243,32 @@ def main():
     torch.cuda.synchronize()
     adv_us = 1000.0 * e0.elapsed_time(e1) / K
 
+    # Saguaro draft reshaping (top-5 of every needed draft row moved by T ln 0.5) on a scratch
+    # copy of the draft logits, timed alone with events on the same stream
+    sag = None
+    if tau is None and w.D > 0:
+        scratch = drfs[0].clone()
+        sag_args = (1 if w.dtype == "bf16" else 0, P(scratch), P(lens), P(temp), w.B, w.D, w.V,
+                    0.5, 5, sp)
+        for _ in range(10):
+            if lib.spec_verify_saguaro_reshape(*sag_args) != 0:
+                raise RuntimeError("spec_verify_saguaro_reshape failed")
+        torch.cuda.synchronize()
+        ks = min(K, 200)
+        e0.record(stream)
+        for _ in range(ks):
+            lib.spec_verify_saguaro_reshape(*sag_args)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sag_us = 1000.0 * e0.elapsed_time(e1) / ks
+        draft_rows = int(sum(int(w.lens[b]) for b in range(w.B) if w.temperature[b] > 0))
+        sag_bytes = draft_rows * w.V * w.elem_bytes
+        sag = {"us_per_call": sag_us, "k": 5, "factor": 0.5, "draft_rows": draft_rows,
+               "gbps": sag_bytes / (sag_us * 1e-6) / 1e9,
+               "note": "spec_verify_saguaro_reshape alone (not part of the step): reads every "
+                       "needed draft row twice (maxima, then the filtered top-5) and rewrites its "
+                       "top-5 logits; gbps counts one read"}
+
     gbps = alg_bytes / (ms_step * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -271,6 +297,7 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": kern_gbps / HBM_PEAK_GBPS,
                      "traffic": read_traffic(args.config, args.seed), "kernel_ms": kern_ms},
         "cpu_baseline": None,
+        "saguaro_reshape": sag,
         "advance": {"us_per_call": adv_us, "W": W,
                     "note": "spec_verify_advance alone (not part of the step): window and "
                             "lengths of the batch moved by AL on the GPU, no host sync"},

@@ -1689,8 +1689,8 @@ __global__ __launch_bounds__(kThreads) void reshape_kernel(E* draft, const int32
   int ti[kMaxTopK];
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) { tv[j] = -INFINITY; ti[j] = -1; }
-  for (int v = tid; v < V; v += kThreads) {
-    const float x = Elem<E>::get(row, size_t(v));
+  // element v with logit x into the thread's sorted list (most elements fail the first test)
+  auto consider = [&](float x, int v) {
     if (tk_better(x, v, tv[kMaxTopK - 1], ti[kMaxTopK - 1])) {
       float cx = x;
       int cv = v;
@@ -1702,7 +1702,64 @@ __global__ __launch_bounds__(kThreads) void reshape_kernel(E* draft, const int32
         }
       }
     }
+  };
+  // Two passes over the row, 16-byte loads, kRowVecs per thread issued together, then the
+  // unaligned or partial tail element by element (the order of the elements does not matter:
+  // ties are broken by index). Pass 1: each thread's maximum; the k-th largest of the
+  // workgroup's maxima, thr, is at most the row's k-th largest logit (k elements reach it), so
+  // pass 2 considers only elements >= thr, and the sorted-list updates become rare.
+  constexpr int kV = Elem<E>::kVec;
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+  const int nvec = aligned ? V / kV : 0;
+  const uint4* vp = reinterpret_cast<const uint4*>(row);
+  auto sweep = [&](auto&& use) {
+    for (int base = 0; base < nvec; base += kRowVecs * kThreads) {
+      uint4 buf[kRowVecs];
+#pragma unroll
+      for (int j = 0; j < kRowVecs; ++j) {
+        const int vi = base + j * kThreads + tid;
+        buf[j] = vi < nvec ? vp[vi] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int j = 0; j < kRowVecs; ++j) {
+        const int vi = base + j * kThreads + tid;
+        if (vi < nvec) {
+#pragma unroll
+          for (int e = 0; e < kV; ++e) use(Elem<E>::lane(buf[j], e), vi * kV + e);
+        }
+      }
+    }
+    for (int v = nvec * kV + tid; v < V; v += kThreads) use(Elem<E>::get(row, size_t(v)), v);
+  };
+  float mx = -INFINITY;
+  int has = -1;                                    // some element seen (all may be -inf)
+  sweep([&](float x, int v) { if (has < 0 || x > mx) { mx = x; has = v; } });
+  __shared__ float smax[kWaves][kMaxTopK];
+  __shared__ float sthr;
+  for (int r = 0; r < k; ++r) {                    // the wavefront's k largest maxima
+    float hv = mx;
+    int hi = has;
+    wave_am(hv, hi);
+    if (hi >= 0 && has == hi) has = -1;            // one lane (unique index) gives its maximum
+    if (lane == 0) smax[wave][r] = hi >= 0 ? hv : -INFINITY;
   }
+  __syncthreads();
+  if (wave == 0) {
+    float cv = lane < kWaves * k ? smax[lane / k][lane % k] : -INFINITY;
+    int ci = lane < kWaves * k ? lane : -1;
+    float kth = -INFINITY;
+    for (int r = 0; r < k; ++r) {
+      float hv = cv;
+      int hi = ci;
+      wave_am(hv, hi);
+      if (hi >= 0 && ci == hi) ci = -1;
+      kth = hv;
+    }
+    if (lane == 0) sthr = kth;
+  }
+  __syncthreads();
+  const float thr = sthr;
+  sweep([&](float x, int v) { if (x >= thr) consider(x, v); });
   __shared__ float sval[kWaves][kMaxTopK];
   __shared__ int sidx[kWaves][kMaxTopK];
   for (int r = 0; r < k; ++r) {                    // the wavefront's top k, best first
