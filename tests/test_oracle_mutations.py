@@ -215,3 +215,53 @@ def test_advance_pin_passes_on_the_oracle():
 ])
 def test_advance_mutations_are_caught(old, new):
     assert not pin_advance_suffix(_mutant_advance(old, new)), new
+
+
+# ---------------------------------------------------------------- Saguaro reshaping
+
+saguaro_mod = importlib.import_module("oracle.saguaro")
+
+
+def pin_saguaro(reshape, top_k):
+    """Tie-heavy rows: the changed tokens are the brute-force top k; in probability space the
+    row becomes q with its top k scaled by c and renormalised."""
+    rng = np.random.default_rng(10)
+    B, D, V, k, c = 4, 2, 60, 5, 0.4
+    draft = rng.integers(-3, 4, (B, D, V)).astype(np.float32)
+    T = np.array([1.0, 0.5, 2.0, 1.5], np.float32)
+    out = reshape(draft, "f32", None, T, c, k)
+    for b in range(B):
+        for i in range(D):
+            row = draft[b, i]
+            want = [j for _, j in sorted((-float(v), j) for j, v in enumerate(row))][:k]
+            if sorted(top_k(row, k).tolist()) != sorted(want):
+                return False
+            q = scipy.special.softmax(row.astype(np.float64) / T[b])
+            q[want] *= c
+            q /= q.sum()
+            got = scipy.special.softmax(out[b, i].astype(np.float64) / T[b])
+            if not np.allclose(got, q, rtol=2e-6, atol=1e-12):
+                return False
+    return True
+
+
+def test_saguaro_pin_passes_on_the_oracle():
+    assert pin_saguaro(saguaro_mod.reshape_draft, saguaro_mod.top_k_indices)
+
+
+def _mutant_saguaro(old, new):
+    src = inspect.getsource(saguaro_mod)
+    assert old in src, old
+    ns = {"__name__": "saguaro_mutant"}
+    exec(src.replace(old, new), ns)
+    return ns["reshape_draft"], ns["top_k_indices"]
+
+
+@pytest.mark.parametrize("old,new", [
+    ("order = np.lexsort((idx, -row.astype(np.float64)))",
+     "order = np.lexsort((-idx, -row.astype(np.float64)))"),               # ties to the highest
+    ("new = (vals[sel] + delta)", "new = (vals[sel] - delta)"),            # shift sign
+    ("delta = np.float32(np.float32(temperature[b]) * lnf)", "delta = lnf"),  # temperature dropped
+])
+def test_saguaro_mutations_are_caught(old, new):
+    assert not pin_saguaro(*_mutant_saguaro(old, new)), new
