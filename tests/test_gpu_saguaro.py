@@ -29,7 +29,11 @@ def _reshape_on_gpu(w, factor, k):
 @pytest.mark.parametrize("cfg,kw,factor,k", [
     ("c3", dict(B=24), 0.5, 5), ("c3", dict(B=8, V=1000), 0.05, 8), ("c3", dict(B=8, V=7), 0.3, 5),
     ("c2", dict(B=8), 0.5, 1), ("c2", dict(B=6, V=100), 0.9, 8), ("c4", dict(B=40), 0.25, 5),
-    ("c5", dict(B=48), 0.5, 5)])
+    ("c5", dict(B=48), 0.5, 5),
+    # rows that are not 16-byte multiples, and rows beyond one workgroup's registers: the
+    # two-sweep kernel that reads the row twice
+    ("c3", dict(B=6, V=1001), 0.5, 5), ("c3", dict(B=4, V=200003), 0.3, 8),
+    ("c2", dict(B=4, V=70001), 0.7, 4)])
 def test_reshape_matches_oracle(cfg, kw, factor, k):
     w = make(cfg, 70, **kw)
     if cfg == "c5":
