@@ -1523,7 +1523,8 @@ int launch(Params& P, hipStream_t stream) {
     Params Q = P;
     Q.b0 = b0;
     Q.nb = std::min(kRowSlice, P.B - b0);
-    const dim3 grid(unsigned(Q.nchunk), unsigned(2 * Q.nb), unsigned(Q.D + 1));
+    // threshold acceptance reads no draft row: the grid holds the target rows only
+    const dim3 grid(unsigned(Q.nchunk), unsigned((Q.thresh ? 1 : 2) * Q.nb), unsigned(Q.D + 1));
     if (stamped) {
       void* args[] = {&Q};
       if (hipExtLaunchKernel(reinterpret_cast<const void*>(&row_kernel<E>), grid, dim3(kThreads),
