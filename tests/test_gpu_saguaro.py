@@ -68,3 +68,37 @@ def test_reshape_then_verify(cfg, kw):
                               t["temperature"])
     torch.cuda.synchronize()
     G.compare(ref, al.cpu().numpy(), toks.cpu().numpy(), f"{cfg} reshaped")
+
+
+def test_reshape_verify_advance_loop_on_one_stream():
+    """Three steps of a serving loop on one stream with no host synchronisation in between:
+    reshape the draft rows, verify, move the token windows; the windows and lengths equal the
+    oracles' chain on every sequence no step flagged."""
+    from oracle import advance
+    dev = G.device()
+    B, W = 32, 10
+    rng = np.random.default_rng(9)
+    ids0 = rng.integers(0, 1000, (B, W)).astype(np.int32)
+    d_ids = torch.from_numpy(ids0).to(dev)
+    d_len = torch.zeros(B, dtype=torch.int32, device=dev)
+    ref_ids, ref_len = ids0, np.zeros(B, np.int32)
+    excused = np.zeros(B, bool)
+    keep = []
+    for step in range(3):
+        w = make("c5", 80 + step, B=B, V=6007)
+        t = G.to_dev(w, dev)
+        sv.spec_verify_saguaro_reshape(t["draft"], t["lens"], t["temperature"], 0.4, 5)
+        al, toks = sv.spec_verify(t["target"], t["draft"], t["tokens"], t["lens"],
+                                  t["uniforms"], t["temperature"])
+        sv.spec_verify_advance(al, toks, d_ids, d_len)
+        keep.append((t, al, toks))
+        shaped = reshape_draft(w.draft, w.dtype, w.lens, w.temperature, 0.4, 5)
+        dec = (shaped.astype(np.uint32) << np.uint32(16)).view(np.float32)
+        r = verify(w.target_f32(), dec, w.tokens, w.lens, w.uniforms, w.temperature)
+        excused |= r.flagged
+        ref_ids, ref_len = advance(r.accept_len, r.tokens, w.D, ref_ids, ref_len)
+    torch.cuda.synchronize()
+    ok = ~excused
+    assert ok.sum() > 0.9 * B
+    assert np.array_equal(d_ids.cpu().numpy()[ok], ref_ids[ok])
+    assert np.array_equal(d_len.cpu().numpy()[ok], ref_len[ok])
