@@ -102,3 +102,13 @@ def test_reshape_verify_advance_loop_on_one_stream():
     assert ok.sum() > 0.9 * B
     assert np.array_equal(d_ids.cpu().numpy()[ok], ref_ids[ok])
     assert np.array_equal(d_len.cpu().numpy()[ok], ref_len[ok])
+
+
+@pytest.mark.parametrize("T", [1e-3, 1000.0])
+def test_reshape_temperature_extremes(T):
+    """Tiny and huge shifts T ln c (bf16 rounding of the shifted logits included)."""
+    w = make("c3", 73, B=8, V=20011)
+    w.temperature[:] = np.float32(T)
+    got = _reshape_on_gpu(w, 0.5, 5)
+    want = reshape_draft(w.draft, w.dtype, None, w.temperature, 0.5, 5)
+    assert np.array_equal(got, want)

@@ -87,3 +87,13 @@ def test_threshold_batches_beyond_one_grid_slice():
                                        torch.from_numpy(T).to(dev), 0.05)
     torch.cuda.synchronize()
     G.compare(ref, al.cpu().numpy(), out.cpu().numpy(), "B=70000")
+
+
+@pytest.mark.parametrize("T", [1e-3, 0.05, 10.0, 1000.0])
+def test_threshold_temperature_extremes(T):
+    """Near-greedy and near-uniform target distributions: prefix log-scores far from the
+    headline's range."""
+    w = make("c3", 15, B=16, V=20011)
+    w.temperature[:] = np.float32(T)
+    for tau in (1e-6, 0.3):
+        _check(w, tau, f"T={T} tau={tau}")
