@@ -35,11 +35,21 @@ x_0..x_{L-1} and uniforms u[b][0..D]:
     infinite, a draft token outside [0, V) at a position < L) gets AL = 0 and all tokens -1.
 
 Boundary flags (decisions that rounding may legitimately flip): an accept test is flagged when
-|u - r| < 1e-5 (r = p(x)/q(x), unclamped); a sampled final draw is flagged when u_f * Z lies
-within 1e-5 * w_k of either edge of the chosen token's bin [F_{k-1}, F_k); a residual draw is
-flagged when its mass Z = sum max(0, p - q) is below 1e-9: its weights are then differences of
-nearly equal probabilities, which fp64 evaluations of p and q carry with absolute errors of
-1e-15 or more per token, so the rounding decides where the mass lies.
+|u - r| < 1e-5 (r = p(x)/q(x), unclamped); a sampled final draw is flagged when t = u_f * Z lies
+closer to either edge of the chosen token's bin [F_{k-1}, F_k) than max(1e-5 * w_k, ABS_WINDOW),
+with the weights w in probability units (p, q and p - q normalised, Z <= 1).
+
+The absolute part ABS_WINDOW = 1e-12 comes from an error bound, not from the data. Any fp64
+evaluation of the weights carries a relative error of at most EVAL_REL = 1e-13 on each
+probability (an fp64 exponential, its argument and the normalising division, at the
+temperatures used). A residual weight max(0, p_v - q_v) is then off by at most
+EVAL_REL * (p_v + q_v), so every prefix sum F_k and the total Z are off by at most
+EVAL_REL * sum_v (p_v + q_v) = 2 * EVAL_REL = 2e-13 (bonus draws: EVAL_REL * F_k, less). Two
+such evaluations (this oracle and any other) can disagree on t - F_{k-1} or F_k - t by twice
+that, 4e-13; ABS_WINDOW keeps a factor 2.5 above it. A residual draw whose whole mass Z is below
+ABS_WINDOW is therefore always flagged: its weights are differences of nearly equal
+probabilities that the rounding decides. A residual of exactly zero mass (only possible through
+rounding) falls back to a draw from p_j and is flagged too.
 """
 from __future__ import annotations
 
@@ -49,7 +59,8 @@ import math
 import numpy as np
 
 FLAG_TOL = 1e-5
-RESIDUAL_MIN_MASS = 1e-9
+EVAL_REL = 1e-13       # relative error bound of an fp64 evaluation of one probability
+ABS_WINDOW = 1e-12     # absolute final-draw window, probability units (module docstring)
 
 
 @dataclasses.dataclass
@@ -99,11 +110,17 @@ def residual_weights(p: np.ndarray, q: np.ndarray) -> np.ndarray:
     return np.maximum(0.0, p - q)
 
 
+def final_window(wk: float) -> float:
+    """Half-width of the flagged window at each edge of a bin of weight wk (probability units):
+    1e-5 of the bin, but never below the absolute rounding bound ABS_WINDOW."""
+    return max(FLAG_TOL * wk, ABS_WINDOW)
+
+
 def inverse_cdf(w: np.ndarray, u: float):
-    """Draw a token from weights w >= 0 with one uniform u in [0, 1): the smallest k with
-    F_k > u * Z, where F is the running sum in ascending token id and Z = F[-1]. If no k
-    qualifies (only possible through rounding) the last token with positive weight is taken.
-    Returns (token, flagged, F_{k-1}, F_k, Z)."""
+    """Draw a token from weights w >= 0 (probability units) with one uniform u in [0, 1): the
+    smallest k with F_k > u * Z, where F is the running sum in ascending token id and Z = F[-1].
+    If no k qualifies (only possible through rounding) the last token with positive weight is
+    taken. Returns (token, flagged, F_{k-1}, F_k, Z)."""
     F = np.cumsum(w)
     Z = F[-1]
     t = u * Z
@@ -114,9 +131,19 @@ def inverse_cdf(w: np.ndarray, u: float):
         k = int(np.nonzero(w > 0)[0][-1])
     lo = F[k - 1] if k > 0 else 0.0
     hi = F[k]
-    win = FLAG_TOL * w[k]
+    win = final_window(float(w[k]))
     flagged = bool((t - lo) < win or (hi - t) < win)
     return k, flagged, lo, hi, Z
+
+
+def final_window_measure(w: np.ndarray) -> float:
+    """Lebesgue measure of the uniforms u in [0, 1) whose draw from w is flagged: in t = u Z the
+    flagged part of bin k is its first and last final_window(w_k), or the whole bin when it is
+    narrower than both together; divided by Z."""
+    wp = w[w > 0]
+    Z = float(np.sum(w))
+    win = np.maximum(FLAG_TOL * wp, ABS_WINDOW)
+    return float(min(1.0, np.sum(np.minimum(wp, 2.0 * win)) / Z))
 
 
 def accept_window_measure(ratio: float) -> float:
@@ -124,11 +151,6 @@ def accept_window_measure(ratio: float) -> float:
     ratio is flagged. Summed over the tests actually performed it estimates the expected
     number of flagged accept decisions."""
     return max(0.0, min(1.0, ratio + FLAG_TOL) - max(0.0, ratio - FLAG_TOL))
-
-
-# final-sample window: the flagged part of each bin is 1e-5 of its width at each edge, so a
-# sampled final draw is flagged with probability exactly 2e-5 whatever the weights are.
-FINAL_WINDOW_MEASURE = 2.0 * FLAG_TOL
 
 
 # --------------------------------------------------------------------------------------------
@@ -210,11 +232,6 @@ def verify(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray,
         if rejected_at >= 0:
             j = rejected_at
             w = residual_weights(softmax(target[b, j], T), softmax(draft[b, j], T))
-            if w.sum() < RESIDUAL_MIN_MASS:   # mass below what fp64 resolves in p - q
-                res.flagged[b] = True
-                res.flag_measure[b] += 1.0
-            if not np.any(w > 0):
-                w = softmax(target[b, j], T)
             res.final_mode[b] = 2
         else:
             j = L
@@ -222,10 +239,15 @@ def verify(target: np.ndarray, draft: np.ndarray, tokens: np.ndarray,
             res.row_max_t[b, j], res.row_logsum_t[b, j] = mt, lst
             w = softmax(target[b, j], T)
             res.final_mode[b] = 3
+        if not np.any(w > 0):                 # residual of zero mass: rounding only
+            w = softmax(target[b, j], T)
+            res.flagged[b] = True
+            res.flag_measure[b] += 1.0
+        else:
+            res.flag_measure[b] += final_window_measure(w)
         k, fl, _, _, _ = inverse_cdf(w, u_final)
         out[j] = k
         res.flagged[b] |= fl
-        res.flag_measure[b] += FINAL_WINDOW_MEASURE
         res.accept_len[b] = j + 1
         res.final_row[b] = j
     return res

@@ -22,6 +22,12 @@ Readings adopted (the page gives neither the score nor the threshold):
   * Flags: a prefix test is flagged when its log-score lies within 1e-5 * k of ln tau (k terms,
     each an fp32 log-probability on the GPU with error below 1e-5); the final draw is flagged as
     in the standard rule.
+  * Window measure of a prefix test (the expected number of flags, as for the standard rule's
+    accept tests): the draft token x_i is a draw from q_i = softmax(draft_i / T), independent of
+    the earlier positions, so given the score s_{i-1} of the prefix before it, test i is flagged
+    with probability sum_x q_i(x) [|s_{i-1} + log p_i(x) - ln tau| < 1e-5 (i+1)]. Summed over
+    the tests performed it estimates the expected number of flagged tests (tower property). It
+    needs the draft logits the tokens were drawn from; without them each flagged test counts 1.
 """
 from __future__ import annotations
 
@@ -29,14 +35,23 @@ import math
 
 import numpy as np
 
-from .oracle import (FINAL_WINDOW_MEASURE, FLAG_TOL, Result, inverse_cdf, row_is_valid,
+from .oracle import (FLAG_TOL, Result, final_window_measure, inverse_cdf, row_is_valid,
                      softmax, tempered_log_softmax)
 
 
+def prefix_window_measure(lp: np.ndarray, q: np.ndarray, prev: float, log_tau: float,
+                          win: float) -> float:
+    """Probability that test i is flagged given the prefix score `prev` before it: the q-mass of
+    the tokens x whose prefix score prev + lp[x] lies within `win` of ln tau."""
+    return float(np.sum(q[np.abs(prev + lp - log_tau) < win]))
+
+
 def verify_threshold(target: np.ndarray, tokens: np.ndarray, lens, uniforms: np.ndarray,
-                     temperature: np.ndarray, tau: float) -> Result:
+                     temperature: np.ndarray, tau: float, draft: np.ndarray | None = None) -> Result:
     """Threshold acceptance of a batch. target [B][D+1][V] (float32 values), tokens [B][D],
-    lens [B] or None (all D), uniforms [B][D+1], temperature [B], tau >= 0."""
+    lens [B] or None (all D), uniforms [B][D+1], temperature [B], tau >= 0. draft [B][D][V]
+    (optional, never used by the rule): the logits the draft tokens were drawn from, for the
+    window measure of the prefix tests."""
     B, D1, V = target.shape
     D = D1 - 1
     if lens is None:
@@ -75,18 +90,24 @@ def verify_threshold(target: np.ndarray, tokens: np.ndarray, lens, uniforms: np.
         for i in range(L):
             lp, _, _ = tempered_log_softmax(target[b, i], T)
             res.logp_x[b, i] = lp[x[i]]
+            win = FLAG_TOL * (i + 1)
+            if draft is not None:
+                res.flag_measure[b] += prefix_window_measure(lp, softmax(draft[b, i], T),
+                                                             score, log_tau, win)
             score += lp[x[i]]
-            if abs(score - log_tau) < FLAG_TOL * (i + 1):
+            if abs(score - log_tau) < win:
                 res.flagged[b] = True
-                res.flag_measure[b] += 1.0
+                if draft is None:
+                    res.flag_measure[b] += 1.0
             if not score > log_tau:
                 j = i
                 break
             out[i] = x[i]
-        k, fl, _, _, _ = inverse_cdf(softmax(target[b, j], T), float(uniforms[b, D]))
+        w = softmax(target[b, j], T)
+        k, fl, _, _, _ = inverse_cdf(w, float(uniforms[b, D]))
         out[j] = k
         res.flagged[b] |= fl
-        res.flag_measure[b] += FINAL_WINDOW_MEASURE
+        res.flag_measure[b] += final_window_measure(w)
         res.accept_len[b] = j + 1
         res.final_row[b] = j
         res.final_mode[b] = 3
@@ -94,5 +115,6 @@ def verify_threshold(target: np.ndarray, tokens: np.ndarray, lens, uniforms: np.
 
 
 def verify_threshold_workload(w, tau: float) -> Result:
+    """The workload's draft logits are passed for the window measure only."""
     return verify_threshold(w.target_f32(), w.tokens, w.lens if w.lens_given else None,
-                            w.uniforms, w.temperature, tau)
+                            w.uniforms, w.temperature, tau, draft=w.draft_f32())

@@ -40,6 +40,16 @@ def run(w, dev=None, debug=False, workspace=None):
     return tuple(o.cpu().numpy() for o in out)
 
 
+def check_flag_rate(flagged, measure, rows, label=""):
+    """The parity gate on excused rows: the expected number of flagged decisions (the oracle's
+    window measure summed over the decisions taken) is below 1e-4 per row, and the raw count of
+    flagged rows agrees with it (at most 10 times the expectation, or 3 when it is below 0.3:
+    a Poisson count of mean 0.3 exceeds 3 with probability 4e-4)."""
+    assert measure / rows < 1e-4, f"{label}: E[flags/row] = {measure / rows:.2e}"
+    assert flagged <= max(3, 10 * measure), \
+        f"{label}: {flagged} flagged rows against {measure:.3f} expected"
+
+
 def compare(ref, al, toks, label=""):
     """Bit-exact on every row the oracle did not flag. Returns (#flagged, #mismatched flagged)."""
     ok = ~ref.flagged

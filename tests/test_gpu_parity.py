@@ -34,7 +34,7 @@ def _parity(cfg, seeds, **kw):
         measure += float(ref.flag_measure.sum())
     print(f"{cfg}: rows={rows} flagged={flagged} (mismatched among them {mism}) "
           f"E[flags/row]={measure / rows:.2e}", flush=True)
-    assert measure / rows < 1e-4
+    G.check_flag_rate(flagged, measure, rows, cfg)
     return flagged, mism
 
 
@@ -44,10 +44,12 @@ def test_parity_full_size(cfg):
 
 
 def _close_log(a, b, tol=1e-5):
+    """Element by element: |a - b| <= tol * max(1, |b|) wherever the oracle computed b."""
     m = ~np.isnan(b)
     assert np.all(~np.isnan(a[m]))
     d = np.abs(a[m].astype(np.float64) - b[m])
-    assert d.max(initial=0) <= tol * np.maximum(1.0, np.abs(b[m])).max(initial=1), d.max()
+    bound = tol * np.maximum(1.0, np.abs(b[m]))
+    assert np.all(d <= bound), float(np.max(d / bound))
 
 
 @pytest.mark.parametrize("cfg,kw", [("c2", {}), ("c3", {}), ("c5", dict(B=64)),

@@ -155,8 +155,9 @@ def test_ratio_beyond_the_double_range_accepts():
 
 def test_residual_below_fp64_resolution_is_flagged():
     """A rejection where p and q agree except far out in the tail: the residual mass is about
-    1e-12, made of differences of probabilities near 1/2, so the draw is left to rounding and
-    the row is flagged. The same shape with a clear difference is not flagged."""
+    1e-12, below the absolute window (the rounding bound of any fp64 evaluation of the weights),
+    so every uniform is flagged: the draw is left to rounding. The same shape with a clear
+    difference is not flagged."""
     target = np.array([[[0.0, -4e-12, -50.0], [0.0, 0.0, 0.0]]], np.float64)
     draft = np.array([[[0.0, 0.0, -40.0]]], np.float64)
     tokens = np.array([[2]], np.int32)

@@ -265,3 +265,75 @@ def _mutant_saguaro(old, new):
 ])
 def test_saguaro_mutations_are_caught(old, new):
     assert not pin_saguaro(*_mutant_saguaro(old, new)), new
+
+
+# ---------------------------------------------------------------- excusal windows and rounding
+
+from tests import test_oracle_windows as PW  # noqa: E402
+
+
+def _mutant_module(mod, old, new):
+    """A copy of an oracle module with one statement changed (relative imports resolve against
+    the real package)."""
+    src = inspect.getsource(mod)
+    assert old in src, old
+    ns = {"__name__": mod.__name__, "__package__": "oracle"}
+    exec(src.replace(old, new), ns)
+    return ns
+
+
+def _window_pins(ns):
+    return {
+        "accept": lambda: PW.pin_accept_window(ns["verify"]),
+        "accept_measure": lambda: PW.pin_accept_measure(ns["verify"], ns["accept_window_measure"]),
+        "final": lambda: PW.pin_final_window(ns["verify"]),
+        "absolute": lambda: PW.pin_absolute_window(ns["verify"]),
+        "final_measure": lambda: PW.pin_final_measure(ns["inverse_cdf"],
+                                                      ns["final_window_measure"]),
+    }
+
+
+@pytest.mark.parametrize("old,new,catcher", [
+    ("if abs(u - ratio) < FLAG_TOL:", "if abs(u - ratio) < 10 * FLAG_TOL:", "accept"),
+    ("if abs(u - ratio) < FLAG_TOL:", "if abs(u - ratio) < 0.5 * FLAG_TOL:", "accept"),
+    ("if abs(u - ratio) < FLAG_TOL:", "if abs(u - ratio) < 10 * FLAG_TOL:", "accept_measure"),
+    ("min(1.0, ratio + FLAG_TOL) - max(0.0, ratio - FLAG_TOL)",
+     "min(1.0, ratio + 2 * FLAG_TOL) - max(0.0, ratio - 2 * FLAG_TOL)", "accept_measure"),
+    ("return max(FLAG_TOL * wk, ABS_WINDOW)", "return max(10 * FLAG_TOL * wk, ABS_WINDOW)",
+     "final"),
+    ("return max(FLAG_TOL * wk, ABS_WINDOW)", "return max(0.5 * FLAG_TOL * wk, ABS_WINDOW)",
+     "final"),
+    ("return max(FLAG_TOL * wk, ABS_WINDOW)", "return FLAG_TOL * wk", "absolute"),
+    ("ABS_WINDOW = 1e-12", "ABS_WINDOW = 1e-11", "absolute"),
+    ("return max(FLAG_TOL * wk, ABS_WINDOW)", "return max(10 * FLAG_TOL * wk, ABS_WINDOW)",
+     "final_measure"),
+    ("return float(min(1.0, np.sum(np.minimum(wp, 2.0 * win)) / Z))", "return 2.0 * FLAG_TOL",
+     "final_measure"),
+])
+def test_window_mutations_are_caught(old, new, catcher):
+    ns = _mutant_module(oracle_mod, old, new)
+    assert _window_pins(importlib.import_module("oracle.oracle").__dict__)[catcher]()
+    assert not _window_pins(ns)[catcher](), new
+
+
+@pytest.mark.parametrize("old,new,catcher", [
+    ("win = FLAG_TOL * (i + 1)", "win = 10 * FLAG_TOL * (i + 1)", PW.pin_threshold_window),
+    ("win = FLAG_TOL * (i + 1)", "win = 0.5 * FLAG_TOL * (i + 1)", PW.pin_threshold_window),
+    ("score, log_tau, win)", "score + lp[x[i]], log_tau, win)", PW.pin_threshold_measure),
+])
+def test_threshold_window_mutations_are_caught(old, new, catcher):
+    ns = _mutant_module(threshold_mod, old, new)
+    assert catcher(oracle.verify_threshold)
+    assert not catcher(ns["verify_threshold"]), new
+
+
+@pytest.mark.parametrize("old,new", [
+    ("return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)",
+     "return (u >> np.uint32(16)).astype(np.uint16)"),                      # truncation
+    ("return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)",
+     "return ((u + np.uint32(0x8000)) >> np.uint32(16)).astype(np.uint16)"),   # ties away
+])
+def test_bf16_rounding_mutations_are_caught(old, new):
+    ns = _mutant_module(saguaro_mod, old, new)
+    assert PW.pin_bf16_rounding(saguaro_mod._bf16_rne)
+    assert not PW.pin_bf16_rounding(ns["_bf16_rne"]), new

@@ -99,3 +99,13 @@ def test_invalid_rows_are_marked():
     r = verify_threshold_workload(w, 0.01)
     assert r.accept_len[0] == 0 and r.accept_len[1] == 0
     assert np.all(r.tokens[:2] == -1) and np.all(r.accept_len[2:] >= 1)
+
+
+def test_flag_rate_estimator_is_small_on_full_headline_config():
+    """The expected number of flagged decisions of threshold acceptance (prefix tests through
+    the draft tokens' distribution, plus the final draw) is below 1e-4 per row at full size."""
+    from workloads import make
+    for tau in (1e-3, 0.05):
+        w = make("c3", 0)
+        r = verify_threshold_workload(w, tau)
+        assert r.flag_measure.mean() < 1e-4, (tau, r.flag_measure.mean())
