@@ -45,8 +45,9 @@
  *     L_b outside [0, D], T_b negative, NaN or infinite, a draft token outside [0, V) at a
  *     position < L_b.
  *   - A failed launch or allocation returns SV_EHIP / SV_ENOMEM.
- *   - Logits must be finite in every row that is read; other values give unspecified tokens
- *     (never an out-of-bounds access).
+ *   - Logits may be -inf (a masked token: probability 0); every row that is read must hold at
+ *     least one finite logit. NaN or +inf logits give unspecified tokens (never an
+ *     out-of-bounds access).
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H

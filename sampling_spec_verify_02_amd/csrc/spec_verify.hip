@@ -501,7 +501,9 @@ __device__ __forceinline__ void row_chunk(const Params& P, Shared& sm, int b, in
       }
     }
     // Exact redo where the packed max may not be the max: it landed on an fp16 inf / NaN
-    // pattern (|value| >= 2^121), or passed over such a value and the sum overflowed.
+    // pattern (|value| >= 2^121, or a thread whose elements are all -inf), or passed over such a
+    // value and the sum overflowed or became NaN (-inf - -inf). -inf elements (masked tokens)
+    // carry no weight.
     if (!(sum < INFINITY) || !(fabsf(mx) < 0x1p121f)) {
       mx = -INFINITY;
       sum = 0.f;
@@ -513,7 +515,7 @@ __device__ __forceinline__ void row_chunk(const Params& P, Shared& sm, int b, in
               sum = (sum == 0.f) ? 0.f : sum * __builtin_amdgcn_exp2f((mx - x) * k2);
               mx = x;
             }
-            sum += __builtin_amdgcn_exp2f((x - mx) * k2);
+            if (x > -INFINITY) sum += __builtin_amdgcn_exp2f((x - mx) * k2);
           }
         }
       }
@@ -524,7 +526,7 @@ __device__ __forceinline__ void row_chunk(const Params& P, Shared& sm, int b, in
         sum = (sum == 0.f) ? 0.f : sum * __builtin_amdgcn_exp2f((mx - x) * k2);
         mx = x;
       }
-      sum += __builtin_amdgcn_exp2f((x - mx) * k2);
+      if (x > -INFINITY) sum += __builtin_amdgcn_exp2f((x - mx) * k2);
     }
     wave_ms(mx, sum, k2);
     if ((tid & 63) == 0) { sm.red[wave][0] = mx; sm.red[wave][1] = sum; }
@@ -783,12 +785,14 @@ __device__ inline void fill_e2(double* e2, int tid) {
 // 2^(r / 256) = e^u with u = r ln2 / 256, |u| <= a = ln2 / 512, from a cubic: the Taylor cubic
 // with the u^4 term economised by the Chebyshev polynomial T4 (u^4 ~ a^2 u^2 - a^4 / 8, off by
 // at most a^4 / 8), relative error below 2e-14; 2^(k / 256) = e2[k mod 256] * 2^(k div 256).
-// Arguments far below zero give 0 (the integer conversion saturates and ldexp underflows).
+// The argument is first raised to at least -2^30, so that a -inf logit (a masked token), or any
+// argument far below zero, keeps k in int range and gives 0 through ldexp's underflow.
 __device__ inline double exp2k(double y, const double* e2) {
   constexpr double c = 0.0027076061740622863;          // ln2 / 256
   constexpr double a2 = c * c / 4;                     // a^2
   constexpr double q0 = 1.0 - a2 * a2 / 192, q1 = c, q2 = (0.5 + a2 / 24) * c * c,
                    q3 = c * c * c / 6;
+  y = fmax(y, -0x1p30);
   const double kf = __builtin_rint(y);
   const double r = y - kf;
   const int k = int(kf);
