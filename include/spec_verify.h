@@ -67,6 +67,7 @@ typedef enum {
   SV_EHIP = -3,     /* a HIP runtime call or kernel launch failed */
   SV_ENODEV = -4,   /* no usable gfx950 device */
   SV_ENOMEM = -5,   /* workspace allocation failed or caller workspace too small */
+  SV_ESCRATCH = -6, /* spec_verify_noalloc: the problem needs more than its fixed scratch */
 } sv_status;
 
 #define SV_MAX_D 31   /* largest draft length D accepted (positions 0..D fit one 32-bit mask) */
@@ -102,6 +103,22 @@ int spec_verify_ws(int dtype, const void* target_logits, const void* draft_logit
                    const float* temperature, int32_t* out_accept_len,
                    int32_t* out_tokens, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);
+
+/* Same operation as spec_verify_ws, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the workspace is a
+ * fixed file-scope device array of SV_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held until the
+ * process ends. No hipMalloc, hipFree or allocating library routine is called. Problems whose
+ * spec_verify_workspace_bytes(B, D, V) exceeds SV_NOALLOC_SCRATCH_BYTES return SV_ESCRATCH and
+ * enqueue nothing (32 MiB covers, e.g., B = 1024 at D = 1, V = 129280 and B = 512 at D = 7).
+ * Every call on one GPU shares that GPU's scratch: calls whose stream work overlaps on one GPU
+ * race and must be ordered by the caller (one stream, or events). Nothing needs clearing between
+ * calls. dtype: 0 = fp32, 1 = bf16; every other argument as for spec_verify_bf16. */
+#define SV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int spec_verify_noalloc(int dtype, const void* target_logits, const void* draft_logits,
+                        const int32_t* draft_tokens, const int32_t* draft_lens,
+                        const float* uniforms, int B, int D, int V,
+                        const float* temperature, int32_t* out_accept_len,
+                        int32_t* out_tokens, hipStream_t stream);
 
 /* Same operation, also exporting the per-row statistics the kernels computed (for tests).
  * Any export pointer may be NULL. Unused rows hold NaN / -1.

@@ -11,7 +11,8 @@ import os
 LIB_NAME = "libspecverify.so"
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
 
-SV_OK, SV_EINVAL, SV_EDTYPE, SV_EHIP, SV_ENODEV, SV_ENOMEM = 0, -1, -2, -3, -4, -5
+SV_OK, SV_EINVAL, SV_EDTYPE, SV_EHIP, SV_ENODEV, SV_ENOMEM, SV_ESCRATCH = 0, -1, -2, -3, -4, -5, -6
+SV_NOALLOC_SCRATCH_BYTES = 32 << 20
 SV_MAX_D = 31
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
@@ -25,6 +26,7 @@ SIGNATURES = {
     "spec_verify_f32": ([_p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p], _i),
     "spec_verify_workspace_bytes": ([_i, _i, _i], _sz),
     "spec_verify_ws": ([_i, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _sz, _p], _i),
+    "spec_verify_noalloc": ([_i, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p], _i),
     "spec_verify_debug": ([_i, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p], _i),
     "spec_verify_advance": ([_p, _p, _i, _i, _p, _i, _p, _p], _i),
     "spec_verify_threshold": ([_i, _p, _p, _p, _p, _i, _i, _i, _p, ctypes.c_float, _p, _p, _p],

@@ -91,6 +91,24 @@ def spec_verify(target_logits, draft_logits, draft_tokens, draft_lens, uniforms,
     return out_accept_len, out_tokens
 
 
+def spec_verify_noalloc(target_logits, draft_logits, draft_tokens, draft_lens, uniforms,
+                        temperature, out_accept_len, out_tokens):
+    """spec_verify through the entry point that allocates no device memory (its workspace is the
+    library's fixed per-GPU scratch; calls that overlap on one GPU race). The outputs must be
+    given. Returns (accept_len, tokens); enqueued on torch's current stream."""
+    B, D, V, temperature, out_accept_len, out_tokens = _prepare(
+        target_logits, draft_logits, draft_tokens, draft_lens, uniforms, temperature,
+        out_accept_len, out_tokens)
+    rc = lib().spec_verify_noalloc(_DT[target_logits.dtype], _ptr(target_logits),
+                                   _ptr(draft_logits), _ptr(draft_tokens), _ptr(draft_lens),
+                                   _ptr(uniforms), B, D, V, _ptr(temperature),
+                                   _ptr(out_accept_len), _ptr(out_tokens),
+                                   _stream(target_logits.device))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_noalloc")
+    return out_accept_len, out_tokens
+
+
 def spec_verify_threshold(target_logits, draft_tokens, draft_lens, uniforms, temperature, tau,
                           out_accept_len=None, out_tokens=None):
     """Threshold acceptance on the GPU: keep the longest draft prefix whose target probability is

@@ -1464,6 +1464,33 @@ struct Profile {        // optional timing of the kernel: one event pair per cal
 std::mutex g_prof_mutex;
 Profile g_prof;
 
+// Scratch of the entry point that allocates nothing (spec_verify_noalloc): file-scope device
+// memory of a fixed size, one copy on every GPU the library runs on, held until the process
+// ends. In host code `scratch` only names the symbol; its device address on the current device
+// comes from hipGetSymbolAddress, taken once per device and kept here. Every call on a device
+// shares that device's copy, so calls that overlap on one GPU race (each call writes every part
+// of it that it reads, so nothing needs clearing between calls).
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mutex;
+std::map<int, void*> g_scratch;      // device -> device address of that device's scratch
+
+int scratch_address(void** out) {
+  int dev = 0, count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return SV_ENODEV;
+  if (hipGetDevice(&dev) != hipSuccess) return SV_ENODEV;
+  std::lock_guard<std::mutex> g(g_scratch_mutex);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return SV_EHIP;
+    it = g_scratch.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return SV_OK;
+}
+
 int check_args(const void* t, const void* d, const int32_t* tok, const float* u, const float* temp,
                int32_t* ol, int32_t* ot, int B, int D, int V, bool need_draft = true) {
   if (B <= 0 || D < 0 || V <= 0 || D > SV_MAX_D) return SV_EINVAL;
@@ -1880,6 +1907,24 @@ int spec_verify_ws(int dtype, const void* target_logits, const void* draft_logit
                  nullptr, nullptr, stream);
 }
 
+int spec_verify_noalloc(int dtype, const void* target_logits, const void* draft_logits,
+                        const int32_t* draft_tokens, const int32_t* draft_lens,
+                        const float* uniforms, int B, int D, int V, const float* temperature,
+                        int32_t* out_accept_len, int32_t* out_tokens, hipStream_t stream) {
+  if (dtype != 0 && dtype != 1) return SV_EDTYPE;
+  const int rc = sv::check_args(target_logits, draft_logits, draft_tokens, uniforms, temperature,
+                                out_accept_len, out_tokens, B, D, V);
+  if (rc != SV_OK) return rc;
+  const size_t need = sv::workspace_bytes(B, D, V);
+  if (need == 0 || need > size_t(SV_NOALLOC_SCRATCH_BYTES)) return SV_ESCRATCH;
+  void* ws = nullptr;
+  const int rs = sv::scratch_address(&ws);
+  if (rs != SV_OK) return rs;
+  return sv::run(dtype, target_logits, draft_logits, draft_tokens, draft_lens, uniforms, B, D,
+                 V, temperature, out_accept_len, out_tokens, ws, size_t(SV_NOALLOC_SCRATCH_BYTES),
+                 nullptr, nullptr, nullptr, stream);
+}
+
 int spec_verify_debug(int dtype, const void* target_logits, const void* draft_logits,
                       const int32_t* draft_tokens, const int32_t* draft_lens,
                       const float* uniforms, int B, int D, int V, const float* temperature,
@@ -1921,6 +1966,8 @@ const char* spec_verify_strerror(int code) {
     case SV_EHIP: return "HIP runtime error";
     case SV_ENODEV: return "no usable GPU device";
     case SV_ENOMEM: return "workspace allocation failed or workspace too small";
+    case SV_ESCRATCH:
+      return "problem needs more workspace than spec_verify_noalloc's fixed scratch holds";
     default: return "unknown status";
   }
 }

@@ -43,7 +43,7 @@ def test_static_queries():
     assert lib.spec_verify_workspace_bytes(4, -1, 10) == 0
     assert lib.spec_verify_workspace_bytes(4, _lib.SV_MAX_D + 1, 10) == 0
     assert lib.spec_verify_workspace_bytes(4, 2, 0) == 0
-    for code in (0, -1, -2, -3, -4, -5, 7):
+    for code in (0, -1, -2, -3, -4, -5, -6, 7):
         assert isinstance(_lib.strerror(code), str)
 
 
@@ -55,10 +55,12 @@ def _call(fn, B=2, D=3, V=100, t=FAKE, d=FAKE, tok=FAKE, u=FAKE, temp=FAKE, ol=F
     lib = _lib.lib()
     if fn == "ws":
         return lib.spec_verify_ws(1, t, d, tok, NUL, u, B, D, V, temp, ol, ot, FAKE, 1 << 30, NUL)
+    if fn == "noalloc":
+        return lib.spec_verify_noalloc(1, t, d, tok, NUL, u, B, D, V, temp, ol, ot, NUL)
     return getattr(lib, fn)(t, d, tok, NUL, u, B, D, V, temp, ol, ot, NUL)
 
 
-@pytest.mark.parametrize("fn", ["spec_verify_bf16", "spec_verify_f32", "ws"])
+@pytest.mark.parametrize("fn", ["spec_verify_bf16", "spec_verify_f32", "ws", "noalloc"])
 def test_bad_arguments_return_einval(fn):
     E = _lib.SV_EINVAL
     assert _call(fn, B=0) == E
@@ -85,6 +87,21 @@ def test_bad_dtype_and_workspace():
     assert lib.spec_verify_ws(1, *args, ctypes.c_void_p(4096 + 8), 1 << 30, NUL) == _lib.SV_ENOMEM
 
 
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """The no-allocation entry point refuses, before any device call, a problem whose workspace
+    exceeds its fixed scratch; the limit is the one the header states."""
+    lib = _lib.lib()
+    assert "SV_NOALLOC_SCRATCH_BYTES (32u << 20)" in open(HEADER).read()
+    assert _lib.SV_NOALLOC_SCRATCH_BYTES == 32 << 20
+    for B, D, V in ((4096, 1, 129280), (2048, 7, 129280), (100000, 3, 32000)):
+        assert lib.spec_verify_workspace_bytes(B, D, V) > _lib.SV_NOALLOC_SCRATCH_BYTES
+        assert _call("noalloc", B=B, D=D, V=V) == _lib.SV_ESCRATCH
+    assert lib.spec_verify_noalloc(7, FAKE, FAKE, FAKE, NUL, FAKE, 2, 3, 100, FAKE, FAKE, FAKE,
+                                   NUL) == _lib.SV_EDTYPE
+    assert lib.spec_verify_workspace_bytes(1024, 1, 129280) <= _lib.SV_NOALLOC_SCRATCH_BYTES
+    assert lib.spec_verify_workspace_bytes(512, 7, 129280) <= _lib.SV_NOALLOC_SCRATCH_BYTES
+
+
 def test_d0_allows_null_draft_pointers():
     lib = _lib.lib()
     # D = 0: draft logits and tokens are not needed; with no device the call ends in ENODEV
@@ -99,6 +116,7 @@ def test_no_device_is_reported():
         pytest.skip("a device is present: this host-only case would launch")
     assert _call("spec_verify_bf16") == _lib.SV_ENODEV
     assert _call("spec_verify_f32") == _lib.SV_ENODEV
+    assert _call("noalloc") == _lib.SV_ENODEV
 
 
 def test_advance_bad_arguments():
