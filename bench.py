@@ -266,8 +266,8 @@ def main():
         sag = {"us_per_call": sag_us, "k": 5, "factor": 0.5, "draft_rows": draft_rows,
                "gbps": sag_bytes / (sag_us * 1e-6) / 1e9,
                "note": "spec_verify_saguaro_reshape alone (not part of the step): reads every "
-                       "needed draft row twice (maxima, then the filtered top-5) and rewrites its "
-                       "top-5 logits; gbps counts one read"}
+                       "needed draft row once (one workgroup per 32 KB chunk, the chunks' top-5 "
+                       "merged by the row's last chunk) and rewrites its top-5 logits"}
 
     gbps = alg_bytes / (ms_step * 1e-3) / 1e9
     res = {

@@ -73,9 +73,13 @@ typedef enum {
 #define SV_MAX_D 31   /* largest draft length D accepted (positions 0..D fit one 32-bit mask) */
 
 /* bf16 logits (bit patterns of bfloat16, 2 bytes each). Returns SV_OK or a negative sv_status.
- * Uses a library-owned workspace on the current device, allocated on first use and grown
- * when a larger problem arrives (hipMalloc; calls on one device are serialized by a mutex
- * while they enqueue). */
+ * Uses a library-owned workspace, one per (current device, stream) that calls the plain entry
+ * points, allocated on first use and grown when a larger problem arrives. Growth is
+ * stream-ordered (hipFreeAsync of the old buffer and hipMallocAsync of the new one on `stream`),
+ * so the host never waits; on a stream under graph capture a call that would need to grow the
+ * workspace returns SV_ENOMEM and enqueues nothing (make a first call before the capture, or use
+ * spec_verify_ws). Each buffer is held until spec_verify_release(stream) or the end of the
+ * process. Calls on one device are serialized by a mutex while they enqueue. */
 int spec_verify_bf16(const void* target_logits, const void* draft_logits,
                      const int32_t* draft_tokens, const int32_t* draft_lens,
                      const float* uniforms, int B, int D, int V,
@@ -167,12 +171,29 @@ int spec_verify_threshold(int dtype, const void* target_logits, const int32_t* d
  *   (NULL: all D) and temperature [B] device as for spec_verify. Greedy sequences, rows at
  *   positions >= L_b and sequences with an invalid length or temperature are left unchanged.
  *   factor in (0, 1]; k in [1, 8] (the page's choice is 5; k > V reshapes every token).
+ * Each needed row is read once, in units; the units' candidates meet in a workspace: the
+ * library-owned one of (current device, stream), allocated on first use and grown in stream
+ * order like spec_verify_bf16's (refused with SV_ENOMEM under graph capture), held until
+ * spec_verify_release(stream).
  * Returns SV_EINVAL (factor or k out of range, bad sizes, NULL draft_logits with D > 0 or NULL
- * temperature), SV_EDTYPE, SV_ENODEV or SV_EHIP, enqueueing nothing on an argument error. Logits
- * must be finite in the rows it reads. Nothing is allocated or synchronised. */
+ * temperature), SV_EDTYPE, SV_ENODEV, SV_ENOMEM or SV_EHIP, enqueueing nothing on an argument
+ * error. Logits must be finite in the rows it reads. Nothing is synchronised. */
 int spec_verify_saguaro_reshape(int dtype, void* draft_logits, const int32_t* draft_lens,
                                 const float* temperature, int B, int D, int V, float factor,
                                 int k, hipStream_t stream);
+
+/* Bytes of device workspace spec_verify_saguaro_reshape_ws needs for shape (B, D, V) (0 on bad
+ * sizes). */
+size_t spec_verify_saguaro_workspace_bytes(int B, int D, int V);
+
+/* spec_verify_saguaro_reshape with a caller-provided device workspace of at least
+ * spec_verify_saguaro_workspace_bytes(B, D, V) bytes, 256-byte aligned (SV_ENOMEM otherwise;
+ * NULL gives SV_EINVAL). Nothing is allocated. The workspace needs no initialisation (each call
+ * writes every part it reads) and must not be used by two calls whose stream work overlaps. */
+int spec_verify_saguaro_reshape_ws(int dtype, void* draft_logits, const int32_t* draft_lens,
+                                   const float* temperature, int B, int D, int V, float factor,
+                                   int k, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
 
 /* Epilogue of a verification step, on the GPU with no host synchronisation ("Accélérer Sonar
  * par la Spéculation", section "Calendrier MTP pour un jeton unique": the target's input tokens
@@ -194,6 +215,14 @@ int spec_verify_saguaro_reshape(int dtype, void* draft_logits, const int32_t* dr
  * or W <= 0 (enqueueing nothing), SV_ENODEV without a device, SV_EHIP for a failed launch. */
 int spec_verify_advance(const int32_t* accept_len, const int32_t* tokens, int B, int D,
                         int32_t* input_ids, int W, int32_t* seq_len, hipStream_t stream);
+
+/* Releases the library-owned workspaces of the plain entry points (verification and Saguaro
+ * reshaping) for (current device, stream),
+ * in stream order (hipFreeAsync on `stream`: the buffer is freed after the stream's earlier
+ * work). Call it before destroying a stream that called spec_verify_bf16 / _f32 /
+ * _threshold / _saguaro_reshape; a later call on the stream allocates again. Returns SV_OK (also when the stream
+ * holds no buffer), SV_ENODEV without a device, SV_EHIP if the free fails. */
+int spec_verify_release(hipStream_t stream);
 
 /* Static text for a status code. */
 const char* spec_verify_strerror(int code);

@@ -32,8 +32,12 @@ SIGNATURES = {
     "spec_verify_threshold": ([_i, _p, _p, _p, _p, _i, _i, _i, _p, ctypes.c_float, _p, _p, _p],
                               _i),
     "spec_verify_saguaro_reshape": ([_i, _p, _p, _p, _i, _i, _i, ctypes.c_float, _i, _p], _i),
+    "spec_verify_saguaro_workspace_bytes": ([_i, _i, _i], _sz),
+    "spec_verify_saguaro_reshape_ws": ([_i, _p, _p, _p, _i, _i, _i, ctypes.c_float, _i, _p, _sz,
+                                        _p], _i),
     "spec_verify_strerror": ([_i], ctypes.c_char_p),
     "spec_verify_version": ([], _i),
+    "spec_verify_release": ([_p], _i),
     "spec_verify_profile_start": ([_i], _i),
     "spec_verify_profile_stop": ([_p, _i, _p], _i),
 }

@@ -152,6 +152,17 @@ def workspace_bytes(B: int, D: int, V: int) -> int:
     return int(lib().spec_verify_workspace_bytes(B, D, V))
 
 
+def release(stream=None):
+    """Frees the library workspace held for (current device, `stream`) in stream order
+    (torch's current stream when None); call it before destroying a stream that used the plain
+    entry points."""
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    rc = lib().spec_verify_release(ctypes.c_void_p(stream.cuda_stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "spec_verify_release")
+
+
 def spec_verify_advance(accept_len, tokens, input_ids, seq_len=None):
     """Epilogue of a verification step, on the GPU: each sequence's window of recent tokens
     input_ids [B][W] int32 moves by its AL and takes the emitted tokens at its end; seq_len [B]
@@ -175,11 +186,18 @@ def spec_verify_advance(accept_len, tokens, input_ids, seq_len=None):
     return input_ids, seq_len
 
 
-def spec_verify_saguaro_reshape(draft_logits, draft_lens, temperature, factor, k=5):
+def saguaro_workspace_bytes(B: int, D: int, V: int) -> int:
+    return int(lib().spec_verify_saguaro_workspace_bytes(B, D, V))
+
+
+def spec_verify_saguaro_reshape(draft_logits, draft_lens, temperature, factor, k=5,
+                                workspace=None):
     """Saguaro reshaping of draft logits [B][D][V] (bfloat16 or float32, in place): the top-k
     logits of every needed row move by T ln(factor), so that the row's softmax is q with its
     top k scaled by `factor` and renormalised. draft_lens [B] int32 or None; temperature: [B]
-    float32 tensor or a Python float. Enqueued on torch's current stream."""
+    float32 tensor or a Python float. workspace: optional uint8 GPU tensor of at least
+    saguaro_workspace_bytes(B, D, V) bytes (no initialisation needed); the library's own buffer
+    is used otherwise. Enqueued on torch's current stream."""
     if draft_logits.dim() != 3:
         raise ValueError("draft_logits must be [B][D][V]")
     B, D, V = draft_logits.shape
@@ -192,9 +210,15 @@ def spec_verify_saguaro_reshape(draft_logits, draft_lens, temperature, factor, k
     if not torch.is_tensor(temperature):
         temperature = torch.full((B,), float(temperature), dtype=torch.float32, device=dev)
     _check(temperature, "temperature", torch.float32, (B,), dev)
-    rc = lib().spec_verify_saguaro_reshape(_DT[draft_logits.dtype], _ptr(draft_logits),
-                                           _ptr(draft_lens), _ptr(temperature), B, D, V,
-                                           float(factor), int(k), _stream(dev))
+    if workspace is not None:
+        rc = lib().spec_verify_saguaro_reshape_ws(
+            _DT[draft_logits.dtype], _ptr(draft_logits), _ptr(draft_lens), _ptr(temperature),
+            B, D, V, float(factor), int(k), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(dev))
+    else:
+        rc = lib().spec_verify_saguaro_reshape(_DT[draft_logits.dtype], _ptr(draft_logits),
+                                               _ptr(draft_lens), _ptr(temperature), B, D, V,
+                                               float(factor), int(k), _stream(dev))
     if rc != SV_OK:
         raise SpecVerifyError(rc, "spec_verify_saguaro_reshape")
     return draft_logits

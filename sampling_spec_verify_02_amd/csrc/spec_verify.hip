@@ -1453,8 +1453,11 @@ struct DeviceWorkspace {
   size_t bytes = 0;
 };
 
+// Library-owned workspaces of the plain entry points: one per (device, stream) that has called
+// them, grown in stream order (hipMallocAsync / hipFreeAsync: the host never waits) and held
+// until spec_verify_release(stream) or the end of the process.
 std::mutex g_ws_mutex;
-std::map<std::pair<int, hipStream_t>, DeviceWorkspace> g_ws;   // library buffers per stream
+std::map<std::pair<int, hipStream_t>, DeviceWorkspace> g_ws;
 
 struct Profile {        // optional timing of the kernel: one event pair per call
   std::vector<hipEvent_t> begin, end;
@@ -1610,14 +1613,17 @@ int run(int dtype, const void* target, const void* draft, const int32_t* tokens,
   if (ws == nullptr) {
     DeviceWorkspace& w = g_ws[{dev, stream}];
     if (w.bytes < need) {
-      if (w.ptr) {
-        // earlier calls on this stream may still use the old buffer
-        if (hipStreamSynchronize(stream) != hipSuccess) return SV_EHIP;
-        (void)hipFree(w.ptr);
-        w.ptr = nullptr;
-        w.bytes = 0;
-      }
-      if (hipMalloc(&w.ptr, need) != hipSuccess) { w.ptr = nullptr; return SV_ENOMEM; }
+      // A stream under graph capture would record the allocation into the graph: growth is
+      // refused there (a first call outside the capture, or spec_verify_ws, avoids it).
+      hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return SV_EHIP;
+      if (cap != hipStreamCaptureStatusNone) return SV_ENOMEM;
+      // Stream-ordered: the old buffer is released after this stream's earlier calls have run,
+      // the new one is ready for this call's kernels, and the host does not wait.
+      if (w.ptr && hipFreeAsync(w.ptr, stream) != hipSuccess) return SV_EHIP;
+      w.ptr = nullptr;
+      w.bytes = 0;
+      if (hipMallocAsync(&w.ptr, need, stream) != hipSuccess) { w.ptr = nullptr; return SV_ENOMEM; }
       w.bytes = need;
     }
     ws = w.ptr;
@@ -1696,143 +1702,378 @@ __global__ void __launch_bounds__(kThreads) advance_kernel(const int32_t* __rest
 // sampling: the draft's most likely tokens get their probabilities lowered when the draft is
 // generated). For each needed draft row (sampled sequence, position < L_b) the k largest logits
 // (ties: lowest index) move by delta = T ln c, which multiplies their probabilities under q by c
-// before renormalisation. One workgroup per row: every thread keeps the sorted top kMaxTopK of
-// its elements (strided by the workgroup), each wavefront then extracts its top k by k rounds of
-// a wavefront argmax, and wavefront 0 merges the four lists the same way; k lanes write the new
-// logits (fp32 sum without contraction, then bf16 round-to-nearest-even for bf16 rows).
+// before renormalisation.
+//
+// Each needed row is read once, in units of 8 KB, one wavefront per unit (the four wavefronts of
+// a workgroup never wait for each other): the unit's top k candidates go to the workspace. A
+// second kernel then takes, with one wavefront per row, the row's top k from its units'
+// candidates by k rounds of a wavefront argmax and writes the k new logits.
 constexpr int kMaxTopK = 8;
 
 __device__ inline bool tk_better(float a, int ia, float b, int ib) {
   return ib < 0 || a > b || (a == b && ia < ib);
 }
 
+// A sorted (best first) list of at most kMaxTopK (value, index) pairs; index -1 = empty.
+struct TopList {
+  float v[kMaxTopK];
+  int i[kMaxTopK];
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) { v[j] = -INFINITY; i[j] = -1; }
+  }
+  __device__ __forceinline__ void insert(float x, int ix) {
+    if (ix < 0 || !tk_better(x, ix, v[kMaxTopK - 1], i[kMaxTopK - 1])) return;
+    float cx = x;
+    int ci = ix;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (tk_better(cx, ci, v[j], i[j])) {
+        const float t = v[j]; v[j] = cx; cx = t;
+        const int u = i[j]; i[j] = ci; ci = u;
+      }
+    }
+  }
+  // k rounds of a wavefront argmax over the lists' heads; round r's winner is returned in lane
+  // r (value, index; index -1 when the lists ran out).
+  __device__ __forceinline__ void wave_top(int k, int lane, float& rv, int& ri) {
+    rv = -INFINITY;
+    ri = -1;
+    for (int r = 0; r < k; ++r) {
+      float hv = v[0];
+      int hi = i[0];
+      wave_am(hv, hi);
+      if (hi >= 0 && i[0] == hi) {          // the owner (unique index) drops its head
+#pragma unroll
+        for (int j = 0; j + 1 < kMaxTopK; ++j) { v[j] = v[j + 1]; i[j] = i[j + 1]; }
+        v[kMaxTopK - 1] = -INFINITY;
+        i[kMaxTopK - 1] = -1;
+      }
+      if (lane == r) { rv = hv; ri = hi; }
+    }
+  }
+};
+
+__device__ inline unsigned long long pack_cand(float v, int i) {
+  return ((unsigned long long)uint32_t(i) << 32) | __float_as_uint(v);
+}
+
+// One wavefront per unit of kSagUnitBytes of a row (a quarter of a 32 KB row chunk); the four
+// wavefronts of a workgroup take consecutive units and never wait for each other.
+constexpr int kSagUnitBytes = kRowChunkBytes / kWaves;
+constexpr int kSagVecs = kSagUnitBytes / 16 / 64;          // 16-byte vectors per lane (8)
+constexpr int kSagCap = 128;                               // hits a wavefront keeps in LDS
+constexpr int kSagSlots = 16;                              // candidate slots per unit
+
+// The k-th largest (k <= 8) of the eight maxima of the wavefront's groups of eight lanes, given
+// each lane's value m (every lane gets it). Each group maximum is some lane's value, so at least
+// k lanes hold a value at or above the result.
+__device__ __forceinline__ float group_kth(float m, int k) {
+  float g = fmaxf(m, dpp_float<0x111, 0xf>(m, -INFINITY));    // row_shr:1
+  g = fmaxf(g, dpp_float<0x112, 0xf>(g, -INFINITY));           // row_shr:2
+  g = fmaxf(g, dpp_float<0x114, 0xf>(g, -INFINITY));           // row_shr:4: lane 8q + 7
+  float t8[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    t8[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), 8 * q + 7));
+#pragma unroll
+  for (int pass = 0; pass < 8; ++pass) {           // odd-even transposition sort, descending
+#pragma unroll
+    for (int q = pass & 1; q + 1 < 8; q += 2) {
+      const float h = fmaxf(t8[q], t8[q + 1]), l = fminf(t8[q], t8[q + 1]);
+      t8[q] = h;
+      t8[q + 1] = l;
+    }
+  }
+  float kth = t8[0];
+#pragma unroll
+  for (int q = 1; q < 8; ++q)
+    if (q == k - 1) kth = t8[q];
+  return kth;
+}
+
+// The hits of a 16-byte aligned unit of n elements (PARTIAL: n may be below a full unit),
+// appended to the wavefront's part of shared memory (at most kSagCap kept; their number is
+// returned). The unit is held in registers: vector j of lane l holds unit elements
+// (l + 64 j) kV + e. All loads are issued before any is used: whole vectors with 16-byte loads
+// (a partial unit loads its last, partial vector element by element, and holds -inf past n). Threshold: each group of eight lanes' maximum, and thr = the
+// k-th largest of the eight group maxima (k <= 8); k groups hold an element at or above it, so
+// thr is at most the unit's k-th largest logit and the unit's top k are among its elements
+// >= thr, the hits (appended in any order: ties go by index).
+template <typename E, bool PARTIAL>
+__device__ __forceinline__ int unit_hits(const E* ptr, int n, int a0, int k, int lane, int* nhit,
+                                         float* hv, int* hi) {
+  constexpr int kV = Elem<E>::kVec;
+  const uint4* vp = reinterpret_cast<const uint4*>(ptr);
+  uint4 buf[kSagVecs];
+  if constexpr (!PARTIAL) {
+#pragma unroll
+    for (int j = 0; j < kSagVecs; ++j) buf[j] = load_stream(vp + lane + j * 64);
+  } else {
+    const int nvec = n / kV;                       // whole vectors
+    const uint4 ninf = make_uint4(Elem<E>::kNegInf, Elem<E>::kNegInf, Elem<E>::kNegInf,
+                                  Elem<E>::kNegInf);
+#pragma unroll
+    for (int j = 0; j < kSagVecs; ++j)
+      buf[j] = nvec > 0 ? load_stream(vp + min(lane + j * 64, nvec - 1)) : ninf;
+    // vectors past the end hold -inf (a repeated element must not count twice below)
+#pragma unroll
+    for (int j = 0; j < kSagVecs; ++j)
+      if (lane + j * 64 >= nvec) buf[j] = ninf;
+    const int rem = n - nvec * kV;                 // elements of the partial vector
+    const int jp = (nvec - lane) >> 6;             // the partial vector is lane's vector jp
+    if (rem > 0 && ((nvec - lane) & 63) == 0) {
+      uint32_t w[4] = {Elem<E>::kNegInf, Elem<E>::kNegInf, Elem<E>::kNegInf, Elem<E>::kNegInf};
+#pragma unroll
+      for (int e = 0; e < kV; ++e) {
+        if (e < rem) {
+          const uint32_t x = sizeof(E) == 2
+              ? uint32_t(ld_global(reinterpret_cast<const uint16_t*>(ptr) + nvec * kV + e))
+              : __float_as_uint(ld_global(reinterpret_cast<const float*>(ptr) + nvec * kV + e));
+          if (sizeof(E) == 2) w[e >> 1] = (w[e >> 1] & (0xffffu << ((1 - (e & 1)) * 16))) | (x << ((e & 1) * 16));
+          else w[e] = x;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kSagVecs; ++j)
+        if (j == jp) buf[j] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);               // every load issued before any use
+  // the lane's maximum (a packed max for bf16, exact below 2^121 in magnitude). Where it may
+  // not be the maximum it is replaced by -inf: any value at most the lane's largest element
+  // keeps thr below at most the unit's k-th largest logit (a lower thr only makes more hits).
+  typename Elem<E>::Acc acc = Elem<E>::acc_init();
+#pragma unroll
+  for (int j = 0; j < kSagVecs; ++j) acc = Elem<E>::acc_add(acc, buf[j]);
+  float mx = Elem<E>::acc_value(acc);
+  if (!(fabsf(mx) < 0x1p121f)) mx = -INFINITY;
+  const float thr = group_kth(mx, k);
+  if (lane == 0) *nhit = 0;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < kSagVecs; ++j) {
+    const int e0 = (lane + j * 64) * kV;
+#pragma unroll
+    for (int e = 0; e < kV; ++e) {
+      const float x = Elem<E>::lane(buf[j], e);
+      if ((!PARTIAL || e0 + e < n) && x >= thr) {
+        const int q = atomicAdd(nhit, 1);
+        if (q < kSagCap) { hv[q] = x; hi[q] = a0 + e0 + e; }
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  return __builtin_amdgcn_readfirstlane(*nhit);
+}
+
+// Every element of a unit that is not 16-byte aligned (rows whose byte length is not a multiple
+// of 16) through the lanes' sorted lists; a lane's kV elements of one vector are loaded together.
 template <typename E>
-__global__ __launch_bounds__(kThreads) void reshape_kernel(E* draft, const int32_t* lens,
+__device__ __forceinline__ void unit_scan(const E* ptr, int n, int a0, int lane, TopList& tl) {
+  constexpr int kV = Elem<E>::kVec;
+  for (int j = 0; (j * 64) * kV < n; ++j) {
+    const int e0 = (lane + j * 64) * kV;
+    float x[kV];
+#pragma unroll
+    for (int e = 0; e < kV; ++e) x[e] = Elem<E>::get(ptr, size_t(min(e0 + e, n - 1)));
+#pragma unroll
+    for (int e = 0; e < kV; ++e)
+      if (e0 + e < n) tl.insert(x[e], a0 + e0 + e);
+  }
+}
+
+// Candidates: one wavefront per unit stores, in the unit's kSagSlots slots of the workspace, a
+// set of candidates that holds the unit's top k: its hits when they fit, else its top k (taken
+// from the hits, or from every element when the unit is a row's last or the row is not 16-byte
+// aligned).
+template <typename E>
+__global__ __launch_bounds__(kThreads) void reshape_kernel(const E* draft, const int32_t* lens,
                                                            const float* temperature, int b0,
-                                                           int D, int V, float lnf, int k) {
-  const int i = int(blockIdx.x);
-  const int b = b0 + int(blockIdx.y);
-  const int tid = int(threadIdx.x), lane = tid & 63, wave = tid >> 6;
+                                                           int D, int V, int nunit, int k,
+                                                           unsigned long long* cand) {
+  __shared__ int s_nhit[kWaves];
+  __shared__ float s_hv[kWaves][kSagCap];
+  __shared__ int s_hi[kWaves][kSagCap];
+  const int tid = int(threadIdx.x), lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int u = int(blockIdx.x) * kWaves + wave;   // unit of the row
+  const int i = int(blockIdx.y);
+  const int b = b0 + int(blockIdx.z);
   const int L = lens ? lens[b] : D;
   const float T = temperature[b];
-  if (!seq_valid(L, D, T) || !(T > 0.f) || i >= L) return;     // the same for the workgroup
-  E* row = draft + (size_t(b) * D + i) * size_t(V);
-  float tv[kMaxTopK];
-  int ti[kMaxTopK];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) { tv[j] = -INFINITY; ti[j] = -1; }
-  // element v with logit x into the thread's sorted list (most elements fail the first test)
-  auto consider = [&](float x, int v) {
-    if (tk_better(x, v, tv[kMaxTopK - 1], ti[kMaxTopK - 1])) {
-      float cx = x;
-      int cv = v;
-#pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        if (tk_better(cx, cv, tv[j], ti[j])) {
-          const float t = tv[j]; tv[j] = cx; cx = t;
-          const int u = ti[j]; ti[j] = cv; cv = u;
-        }
-      }
-    }
-  };
-  // Two passes over the row, 16-byte loads, kRowVecs per thread issued together, then the
-  // unaligned or partial tail element by element (the order of the elements does not matter:
-  // ties are broken by index). Pass 1: each thread's maximum; the k-th largest of the
-  // workgroup's maxima, thr, is at most the row's k-th largest logit (k elements reach it), so
-  // pass 2 considers only elements >= thr, and the sorted-list updates become rare.
-  constexpr int kV = Elem<E>::kVec;
-  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
-  const int nvec = aligned ? V / kV : 0;
-  const uint4* vp = reinterpret_cast<const uint4*>(row);
-  auto sweep = [&](auto&& use) {
-    for (int base = 0; base < nvec; base += kRowVecs * kThreads) {
-      uint4 buf[kRowVecs];
-#pragma unroll
-      for (int j = 0; j < kRowVecs; ++j) {
-        const int vi = base + j * kThreads + tid;
-        buf[j] = vi < nvec ? vp[vi] : make_uint4(0u, 0u, 0u, 0u);
-      }
-#pragma unroll
-      for (int j = 0; j < kRowVecs; ++j) {
-        const int vi = base + j * kThreads + tid;
-        if (vi < nvec) {
-#pragma unroll
-          for (int e = 0; e < kV; ++e) use(Elem<E>::lane(buf[j], e), vi * kV + e);
-        }
-      }
-    }
-    for (int v = nvec * kV + tid; v < V; v += kThreads) use(Elem<E>::get(row, size_t(v)), v);
-  };
-  float mx = -INFINITY;
-  int has = -1;                                    // some element seen (all may be -inf)
-  sweep([&](float x, int v) { if (has < 0 || x > mx) { mx = x; has = v; } });
-  __shared__ float smax[kWaves][kMaxTopK];
-  __shared__ float sthr;
-  for (int r = 0; r < k; ++r) {                    // the wavefront's k largest maxima
-    float hv = mx;
-    int hi = has;
-    wave_am(hv, hi);
-    if (hi >= 0 && has == hi) has = -1;            // one lane (unique index) gives its maximum
-    if (lane == 0) smax[wave][r] = hi >= 0 ? hv : -INFINITY;
+  if (!seq_valid(L, D, T) || !(T > 0.f) || i >= L || u >= nunit) return;
+  const size_t rid = size_t(b) * D + i;
+  const E* row = draft + rid * size_t(V);
+  constexpr int ue = kSagUnitBytes / int(sizeof(E));
+  const int a0 = u * ue;
+  const int n = min(ue, V - a0);
+  const E* ptr = row + a0;
+  // The unit's slots: up to kSagSlots candidates (empty slots: index -1) that include its top k.
+  unsigned long long* slot = cand + (rid * size_t(nunit) + u) * kSagSlots;
+  int nh = kSagCap + 1;
+  const bool aligned = (reinterpret_cast<uintptr_t>(ptr) & 15) == 0;
+  if (aligned && n == ue)
+    nh = unit_hits<E, false>(ptr, n, a0, k, lane, &s_nhit[wave], s_hv[wave], s_hi[wave]);
+  else if (aligned)
+    nh = unit_hits<E, true>(ptr, n, a0, k, lane, &s_nhit[wave], s_hv[wave], s_hi[wave]);
+  if (nh <= kSagSlots) {                           // the usual case: the hits themselves
+    if (lane < kSagSlots)
+      slot[lane] = lane < nh ? pack_cand(s_hv[wave][lane], s_hi[wave][lane]) : pack_cand(0.f, -1);
+    return;
   }
-  __syncthreads();
-  if (wave == 0) {
-    float cv = lane < kWaves * k ? smax[lane / k][lane % k] : -INFINITY;
-    int ci = lane < kWaves * k ? lane : -1;
-    float kth = -INFINITY;
-    for (int r = 0; r < k; ++r) {
-      float hv = cv;
-      int hi = ci;
-      wave_am(hv, hi);
-      if (hi >= 0 && ci == hi) ci = -1;
-      kth = hv;
-    }
-    if (lane == 0) sthr = kth;
+  // more hits than slots (many equal logits), or an unaligned unit: its top k
+  TopList tl;
+  tl.clear();
+  if (nh <= kSagCap) {
+    for (int q = lane; q < nh; q += 64) tl.insert(s_hv[wave][q], s_hi[wave][q]);
+  } else {
+    unit_scan<E>(ptr, n, a0, lane, tl);
   }
-  __syncthreads();
-  const float thr = sthr;
-  sweep([&](float x, int v) { if (x >= thr) consider(x, v); });
-  __shared__ float sval[kWaves][kMaxTopK];
-  __shared__ int sidx[kWaves][kMaxTopK];
-  for (int r = 0; r < k; ++r) {                    // the wavefront's top k, best first
-    float hv = tv[0];
-    int hi = ti[0];
-    wave_am(hv, hi);
-    if (hi >= 0 && ti[0] == hi) {                  // the owner drops its head
-#pragma unroll
-      for (int j = 0; j + 1 < kMaxTopK; ++j) { tv[j] = tv[j + 1]; ti[j] = ti[j + 1]; }
-      tv[kMaxTopK - 1] = -INFINITY;
-      ti[kMaxTopK - 1] = -1;
-    }
-    if (lane == 0) { sval[wave][r] = hv; sidx[wave][r] = hi; }
-  }
-  __syncthreads();
-  if (wave != 0) return;
-  float cv = -INFINITY;
-  int ci = -1;
-  if (lane < kWaves * k) { cv = sval[lane / k][lane % k]; ci = sidx[lane / k][lane % k]; }
+  float cv;
+  int ci;
+  tl.wave_top(k, lane, cv, ci);
+  if (lane < kSagSlots) slot[lane] = lane < k ? pack_cand(cv, ci) : pack_cand(0.f, -1);
+}
+
+// Merge: one wavefront per row takes the row's top k from its units' candidates and writes the
+// k new logits (fp32 sum without contraction, then bf16 round-to-nearest-even for bf16 rows).
+// Each lane's best candidate gives a threshold (group_kth: at most the row's k-th largest
+// candidate); the candidates at or above it go to shared memory, and each of them finds its rank
+// by comparing itself with all of them (value, then the lower index first); ranks below k are
+// the row's top k in order. Rows with more candidates than one pass of eight per lane, or more
+// of them at the threshold than shared memory holds, go through the lanes' sorted lists.
+constexpr int kSagMergeCap = 256;
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void reshape_merge_kernel(E* draft, const int32_t* lens,
+                                                                 const float* temperature,
+                                                                 int b0, int nb, int D, int V,
+                                                                 int nunit, float lnf, int k,
+                                                                 const unsigned long long* cand) {
+  __shared__ int s_n[kWaves];
+  __shared__ unsigned long long s_c[kWaves][kSagMergeCap];
+  __shared__ unsigned long long s_top[kWaves][kMaxTopK];
+  const int lane = int(threadIdx.x) & 63;
+  const int wave = uniform(int(threadIdx.x) >> 6);
+  const int r = int(blockIdx.x) * kWaves + wave;   // row of the slice
+  if (r >= nb * D) return;
+  const int b = b0 + r / D, i = r % D;
+  const int L = lens ? lens[b] : D;
+  const float T = temperature[b];
+  if (!seq_valid(L, D, T) || !(T > 0.f) || i >= L) return;
+  const size_t rid = size_t(b) * D + i;
+  const unsigned long long* rc = cand + rid * size_t(nunit) * kSagSlots;
+  const int ncand = nunit * kSagSlots;
   float myv = 0.f;
   int mine = -1;
-  for (int r = 0; r < k; ++r) {                    // the row's top k
-    float hv = cv;
-    int hi = ci;
-    wave_am(hv, hi);
-    if (hi >= 0 && ci == hi) ci = -1;
-    if (lane == r) { myv = hv; mine = hi; }
+  bool done = false;
+  if (ncand <= 8 * 64) {
+    // lane l takes slots 8 l .. 8 l + 7: half a unit's slots, so that every group of eight
+    // lanes holds the hits of four units (a unit's empty slots are its last ones)
+    unsigned long long w[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int q = lane * 8 + t;
+      w[t] = q < ncand ? rc[q] : pack_cand(0.f, -1);
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if (int(uint32_t(w[t] >> 32)) >= 0) m = fmaxf(m, __uint_as_float(uint32_t(w[t])));
+    const float thr = group_kth(m, k);
+    if (lane == 0) s_n[wave] = 0;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (int(uint32_t(w[t] >> 32)) >= 0 && __uint_as_float(uint32_t(w[t])) >= thr) {
+        const int q = atomicAdd(&s_n[wave], 1);
+        if (q < kSagMergeCap) s_c[wave][q] = w[t];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int nh = __builtin_amdgcn_readfirstlane(s_n[wave]);
+    if (nh <= kSagMergeCap) {
+      for (int h = lane; h < nh; h += 64) {
+        const unsigned long long c = s_c[wave][h];
+        const float cv = __uint_as_float(uint32_t(c));
+        const int ci = int(uint32_t(c >> 32));
+        int rank = 0;
+        for (int g = 0; g < nh; ++g) {
+          const unsigned long long o = s_c[wave][g];
+          rank += tk_better(__uint_as_float(uint32_t(o)), int(uint32_t(o >> 32)), cv, ci) &&
+                  int(uint32_t(o >> 32)) != ci;
+        }
+        if (rank < k) s_top[wave][rank] = c;
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (lane < k && lane < nh) {
+        const unsigned long long c = s_top[wave][lane];
+        myv = __uint_as_float(uint32_t(c));
+        mine = int(uint32_t(c >> 32));
+      }
+      done = true;
+    }
+  }
+  if (!done) {
+    TopList tl;
+    tl.clear();
+    for (int q0 = 0; q0 < ncand; q0 += 8 * 64) {   // eight loads in flight per lane
+      unsigned long long w[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int q = q0 + t * 64 + lane;
+        w[t] = q < ncand ? rc[q] : pack_cand(0.f, -1);
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        tl.insert(__uint_as_float(uint32_t(w[t])), int(uint32_t(w[t] >> 32)));
+    }
+    tl.wave_top(k, lane, myv, mine);
   }
   if (lane < k && mine >= 0) {
+    E* row = draft + rid * size_t(V);
     const float sum = __fadd_rn(myv, __fmul_rn(T, lnf));
     if constexpr (sizeof(E) == 2) {
-      const uint32_t u = __float_as_uint(sum);
-      row[mine] = E((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+      const uint32_t w = __float_as_uint(sum);
+      row[mine] = E((w + 0x7fffu + ((w >> 16) & 1u)) >> 16);
     } else {
       row[mine] = E(sum);
     }
   }
 }
 
+// Workspace of the reshaping: the candidates [B*D][nunit][kSagSlots]; every slot the merge reads
+// is written by the same call first, so it needs no initialisation. One layout serves both
+// dtypes (the unit count is fp32's, the larger).
+struct SagLayout {
+  int nunit;
+  size_t total;
+};
+
+inline bool sag_layout(int B, int D, int V, SagLayout& L) {
+  if (B <= 0 || D < 0 || V <= 0 || D > SV_MAX_D) return false;
+  const int ue32 = kSagUnitBytes / 4;
+  L.nunit = int((size_t(V) + ue32 - 1) / ue32);
+  L.total = align256(size_t(B) * size_t(D) * size_t(L.nunit) * kSagSlots *
+                     sizeof(unsigned long long));
+  if (L.total == 0) L.total = 256;
+  return true;
+}
+
+inline size_t sag_workspace_bytes(int B, int D, int V) {
+  SagLayout l;
+  return sag_layout(B, D, V, l) ? l.total : 0;
+}
+
+// Library-owned reshaping workspaces, one per (device, stream), grown in stream order like the
+// verification workspaces and held until spec_verify_release(stream).
+std::map<std::pair<int, hipStream_t>, DeviceWorkspace> g_sag;
+
+// ws == nullptr: the library-owned workspace of (device, stream).
 int saguaro_reshape(int dtype, void* draft, const int32_t* lens, const float* temperature, int B,
-                    int D, int V, float factor, int k, hipStream_t stream) {
+                    int D, int V, float factor, int k, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
   if (dtype != 0 && dtype != 1) return SV_EDTYPE;
   if (B <= 0 || D < 0 || V <= 0 || D > SV_MAX_D || k < 1 || k > kMaxTopK) return SV_EINVAL;
   if (!(factor > 0.f) || !(factor <= 1.f)) return SV_EINVAL;
@@ -1840,20 +2081,55 @@ int saguaro_reshape(int dtype, void* draft, const int32_t* lens, const float* te
   if ((unsigned __int128)B * (unsigned __int128)(D + 1) * (unsigned __int128)V >
       ((unsigned __int128)1 << 60))
     return SV_EINVAL;
-  int count = 0;
+  int dev = 0, count = 0;
   if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return SV_ENODEV;
+  if (hipGetDevice(&dev) != hipSuccess) return SV_ENODEV;
   if (D == 0) return SV_OK;
+  SagLayout lay;
+  sag_layout(B, D, V, lay);
+  if (ws != nullptr && (ws_bytes < lay.total || (reinterpret_cast<uintptr_t>(ws) & 255)))
+    return SV_ENOMEM;
+  const int ue = dtype == 1 ? kSagUnitBytes / 2 : kSagUnitBytes / 4;
+  const int nunit = int((size_t(V) + ue - 1) / ue);
+  if (nunit > 0x7fffffff / 64) return SV_EINVAL;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  if (ws == nullptr) {
+    DeviceWorkspace& w = g_sag[{dev, stream}];
+    if (w.bytes < lay.total) {
+      hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return SV_EHIP;
+      if (cap != hipStreamCaptureStatusNone) return SV_ENOMEM;
+      if (w.ptr && hipFreeAsync(w.ptr, stream) != hipSuccess) return SV_EHIP;
+      w.ptr = nullptr;
+      w.bytes = 0;
+      if (hipMallocAsync(&w.ptr, lay.total, stream) != hipSuccess) { w.ptr = nullptr; return SV_ENOMEM; }
+      w.bytes = lay.total;
+    }
+    ws = w.ptr;
+  }
+  unsigned long long* cand = static_cast<unsigned long long*>(ws);
   const float lnf = float(std::log(double(factor)));
   const int kk = std::min(k, V);
   constexpr int kSlice = 65535;
   for (int b0 = 0; b0 < B; b0 += kSlice) {
-    const dim3 grid(unsigned(D), unsigned(std::min(kSlice, B - b0)));
-    if (dtype == 1)
+    const int nb = std::min(kSlice, B - b0);
+    const dim3 grid(unsigned((nunit + kWaves - 1) / kWaves), unsigned(D), unsigned(nb));
+    const unsigned mgrid = unsigned((size_t(nb) * D + kWaves - 1) / kWaves);
+    if (dtype == 1) {
       hipLaunchKernelGGL(reshape_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
-                         static_cast<uint16_t*>(draft), lens, temperature, b0, D, V, lnf, kk);
-    else
+                         static_cast<const uint16_t*>(draft), lens, temperature, b0, D, V, nunit,
+                         kk, cand);
+      hipLaunchKernelGGL(reshape_merge_kernel<uint16_t>, dim3(mgrid), dim3(kThreads), 0, stream,
+                         static_cast<uint16_t*>(draft), lens, temperature, b0, nb, D, V, nunit,
+                         lnf, kk, cand);
+    } else {
       hipLaunchKernelGGL(reshape_kernel<float>, grid, dim3(kThreads), 0, stream,
-                         static_cast<float*>(draft), lens, temperature, b0, D, V, lnf, kk);
+                         static_cast<const float*>(draft), lens, temperature, b0, D, V, nunit,
+                         kk, cand);
+      hipLaunchKernelGGL(reshape_merge_kernel<float>, dim3(mgrid), dim3(kThreads), 0, stream,
+                         static_cast<float*>(draft), lens, temperature, b0, nb, D, V, nunit, lnf,
+                         kk, cand);
+    }
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
   }
   return SV_OK;
@@ -1950,7 +2226,20 @@ int spec_verify_saguaro_reshape(int dtype, void* draft_logits, const int32_t* dr
                                 const float* temperature, int B, int D, int V, float factor,
                                 int k, hipStream_t stream) {
   return sv::saguaro_reshape(dtype, draft_logits, draft_lens, temperature, B, D, V, factor, k,
-                             stream);
+                             nullptr, 0, stream);
+}
+
+size_t spec_verify_saguaro_workspace_bytes(int B, int D, int V) {
+  return sv::sag_workspace_bytes(B, D, V);
+}
+
+int spec_verify_saguaro_reshape_ws(int dtype, void* draft_logits, const int32_t* draft_lens,
+                                   const float* temperature, int B, int D, int V, float factor,
+                                   int k, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  if (workspace == nullptr) return SV_EINVAL;
+  return sv::saguaro_reshape(dtype, draft_logits, draft_lens, temperature, B, D, V, factor, k,
+                             workspace, workspace_bytes, stream);
 }
 
 int spec_verify_advance(const int32_t* accept_len, const int32_t* tokens, int B, int D,
@@ -1972,7 +2261,22 @@ const char* spec_verify_strerror(int code) {
   }
 }
 
-int spec_verify_version(void) { return 301; }
+int spec_verify_version(void) { return 302; }
+
+int spec_verify_release(hipStream_t stream) {
+  int dev = 0, count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return SV_ENODEV;
+  if (hipGetDevice(&dev) != hipSuccess) return SV_ENODEV;
+  std::lock_guard<std::mutex> lock(sv::g_ws_mutex);
+  int rc = SV_OK;
+  for (auto* m : {&sv::g_ws, &sv::g_sag}) {
+    auto it = m->find({dev, stream});
+    if (it == m->end()) continue;
+    if (it->second.ptr && hipFreeAsync(it->second.ptr, stream) != hipSuccess) rc = SV_EHIP;
+    m->erase(it);
+  }
+  return rc;
+}
 
 int spec_verify_profile_start(int max_calls) {
   if (max_calls <= 0 || max_calls > (1 << 20)) return SV_EINVAL;

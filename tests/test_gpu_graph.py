@@ -1,8 +1,8 @@
 """One serving step captured in a HIP graph and replayed: Saguaro reshaping of the draft rows,
 verification with a caller workspace (spec_verify_ws: no allocation, no synchronisation, no
 memset inside the call), then the epilogue that moves each sequence's token window by AL. The
-step is captured once and replayed three times, with eager work (restoring the inputs) and
-synchronisations between the replays; every replay must equal the eager step and, on rows the
+step (the reshaping also with a caller workspace) is captured once and replayed three times,
+with eager work (restoring the inputs) and synchronisations between the replays; every replay must equal the eager step and, on rows the
 oracle does not flag, the oracles' chain (reshape, verify, advance)."""
 import numpy as np
 import pytest
@@ -38,6 +38,7 @@ def test_captured_step_replays_match_eager_and_oracle(cfg, kw):
     t = G.to_dev(w, dev)
     pristine = t["draft"].clone()
     ws = torch.empty(sv.workspace_bytes(w.B, w.D, w.V), dtype=torch.uint8, device=dev)
+    sag_ws = torch.empty(sv.saguaro_workspace_bytes(w.B, w.D, w.V), dtype=torch.uint8, device=dev)
     al = torch.empty(w.B, dtype=torch.int32, device=dev)
     toks = torch.empty((w.B, w.D + 1), dtype=torch.int32, device=dev)
     d_ids = torch.empty((w.B, W), dtype=torch.int32, device=dev)
@@ -52,7 +53,8 @@ def test_captured_step_replays_match_eager_and_oracle(cfg, kw):
         toks.fill_(-7)
 
     def step():
-        sv.spec_verify_saguaro_reshape(t["draft"], t["lens"], t["temperature"], 0.4, 5)
+        sv.spec_verify_saguaro_reshape(t["draft"], t["lens"], t["temperature"], 0.4, 5,
+                                       workspace=sag_ws)
         sv.spec_verify(t["target"], t["draft"], t["tokens"], t["lens"], t["uniforms"],
                        t["temperature"], out_accept_len=al, out_tokens=toks, workspace=ws)
         sv.spec_verify_advance(al, toks, d_ids, d_len)

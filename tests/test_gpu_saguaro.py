@@ -30,10 +30,11 @@ def _reshape_on_gpu(w, factor, k):
     ("c3", dict(B=24), 0.5, 5), ("c3", dict(B=8, V=1000), 0.05, 8), ("c3", dict(B=8, V=7), 0.3, 5),
     ("c2", dict(B=8), 0.5, 1), ("c2", dict(B=6, V=100), 0.9, 8), ("c4", dict(B=40), 0.25, 5),
     ("c5", dict(B=48), 0.5, 5),
-    # rows that are not 16-byte multiples, and rows beyond one workgroup's registers: the
-    # two-sweep kernel that reads the row twice
+    # rows that are not 16-byte multiples (element loads), rows of many chunks with a ragged
+    # last chunk, a chunk smaller than k
     ("c3", dict(B=6, V=1001), 0.5, 5), ("c3", dict(B=4, V=200003), 0.3, 8),
-    ("c2", dict(B=4, V=70001), 0.7, 4)])
+    ("c2", dict(B=4, V=70001), 0.7, 4), ("c3", dict(B=5, V=2 * 16384 + 3), 0.5, 8),
+    ("c2", dict(B=5, V=3 * 8192 + 5), 0.5, 8)])
 def test_reshape_matches_oracle(cfg, kw, factor, k):
     w = make(cfg, 70, **kw)
     if cfg == "c5":
@@ -42,6 +43,48 @@ def test_reshape_matches_oracle(cfg, kw, factor, k):
     want = reshape_draft(w.draft, w.dtype, w.lens if w.lens_given else None, w.temperature,
                          factor, k)
     assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+
+
+def test_reshape_top_k_across_chunk_boundaries():
+    """The row's top k spread over several chunks, with ties across chunk boundaries and
+    inside one chunk (lowest indices win), bf16 and fp32."""
+    for cfg, ce in (("c3", 16384), ("c2", 8192)):
+        w = make(cfg, 74, B=3, V=4 * ce + 17)
+        rows = w.draft.reshape(-1, w.V)
+        hi = np.float32(40.0)
+        val = (np.uint16(np.float32(hi).view(np.uint32) >> 16) if w.dtype == "bf16" else hi)
+        for r in range(rows.shape[0]):
+            for pos in (ce - 1, ce, 2 * ce + 5, 4 * ce + 16, 7, 3 * ce - 1):
+                rows[r, pos] = val
+        got = _reshape_on_gpu(w, 0.5, 5)
+        want = reshape_draft(w.draft, w.dtype, None, w.temperature, 0.5, 5)
+        assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), cfg
+
+
+def test_reshape_caller_workspace_is_reusable():
+    """spec_verify_saguaro_reshape_ws: one workspace, filled with garbage first, serves calls of
+    different shapes in a row on one stream, matching the oracle each time."""
+    dev = G.device()
+    loads = [make("c3", 75, B=6, V=40000), make("c2", 76, B=8, V=9000),
+             make("c5", 77, B=12, V=20011)]
+    size = max(sv.saguaro_workspace_bytes(w.B, w.D, w.V) for w in loads)
+    ws = torch.randint(0, 256, (size,), dtype=torch.uint8, device=dev)
+    for rep in range(2):
+        outs = []
+        for w in loads:
+            d = G.logits_to_dev(w.draft, w.dtype, dev)
+            lens = torch.from_numpy(w.lens).to(dev) if w.lens_given else None
+            sv.spec_verify_saguaro_reshape(d, lens, torch.from_numpy(w.temperature).to(dev),
+                                           0.5, 5, workspace=ws)
+            outs.append(d)
+        torch.cuda.synchronize()
+        for w, d in zip(loads, outs):
+            got = d.cpu()
+            got = got.view(torch.int16).numpy().view(np.uint16) if w.dtype == "bf16" \
+                else got.numpy()
+            want = reshape_draft(w.draft, w.dtype, w.lens if w.lens_given else None,
+                                 w.temperature, 0.5, 5)
+            assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), (rep, w.name)
 
 
 def test_reshape_ties_take_lowest_indices():
