@@ -787,15 +787,20 @@ __device__ inline void fill_e2(double* e2, int tid) {
 // at most a^4 / 8), relative error below 2e-14; 2^(k / 256) = e2[k mod 256] * 2^(k div 256).
 // The argument is first raised to at least -2^30, so that a -inf logit (a masked token), or any
 // argument far below zero, keeps k in int range and gives 0 through ldexp's underflow.
+// k = rint(y) comes from adding 1.5 * 2^52: the sum's low 32 bits hold k (two's complement, for
+// |y| < 2^31) and subtracting the constant again gives kf exactly, with no conversion
+// instruction.
 __device__ inline double exp2k(double y, const double* e2) {
   constexpr double c = 0.0027076061740622863;          // ln2 / 256
   constexpr double a2 = c * c / 4;                     // a^2
   constexpr double q0 = 1.0 - a2 * a2 / 192, q1 = c, q2 = (0.5 + a2 / 24) * c * c,
                    q3 = c * c * c / 6;
+  constexpr double kRound = 6755399441055744.0;       // 1.5 * 2^52
   y = fmax(y, -0x1p30);
-  const double kf = __builtin_rint(y);
+  const double t = y + kRound;
+  const double kf = t - kRound;
   const double r = y - kf;
-  const int k = int(kf);
+  const int k = int(uint32_t(__double_as_longlong(t)));
   const double p = fma(fma(fma(r, q3, q2), r, q1), r, q0);
   return ldexp(e2[k & 255] * p, k >> 8);
 }
