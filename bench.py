@@ -56,21 +56,42 @@ def valid_row_bytes(w, threshold=False) -> int:
     return rows * w.V * w.elem_bytes, rows
 
 
+def fetched_row_bytes(w, al, cuts, threshold=False) -> int:
+    """Logit bytes the staged row launches read for this batch, given each sequence's AL from the
+    call: launch s reads positions [cuts[s], cuts[s+1]) of a sequence unless its first rejection
+    j lies before cuts[s] (then the rows past j are skipped)."""
+    rows = 0
+    for b in range(w.B):
+        L = int(w.lens[b])
+        if al[b] < 1:
+            continue                      # invalid row: nothing past the check is read
+        j = int(al[b]) - 1
+        stop = cuts[-1]
+        for s in range(1, len(cuts) - 1):
+            if j < cuts[s]:
+                stop = cuts[s]
+                break
+        last = min(L, stop - 1)
+        draft = not (w.temperature[b] == 0 or threshold)
+        rows += (last + 1) + (min(last + 1, L) if draft else 0)
+    return rows * w.V * w.elem_bytes
+
+
 def source_digest() -> str:
     return hashlib.sha256(open(SRC, "rb").read()).hexdigest()
 
 
 def read_traffic(config: str, seed: int):
-    """HBM bytes per launch of the row-statistics kernel from the committed rocprofv3 PMC
-    summary, or None if the kernel source changed since the counters were taken or the
-    counters were taken on another workload."""
+    """HBM bytes of a call's row phase (its row launches, FETCH_SIZE and WRITE_SIZE summed over
+    them) from the committed rocprofv3 PMC summary, or None if the kernel source changed since
+    the counters were taken or the counters were taken on another workload."""
     try:
         t = json.load(open(TRAFFIC))
     except (OSError, ValueError):
         return None
     if t.get("source_sha256") != source_digest() or (config, seed) != ("c3", 0):
         return None
-    return t.get("traffic_bytes_per_launch")
+    return t.get("traffic_bytes_row_phase")
 
 
 def cpu_baseline(w, seconds: float, tau=None):
@@ -224,7 +245,14 @@ def main():
     if rc != 0:
         raise RuntimeError(sv.strerror(rc))
     kern_ms = float(np.mean(np.array(durs[:n.value], dtype=np.float64)))
-    kern_gbps = alg_bytes / (kern_ms * 1e-3) / 1e9
+    # the row launches of a call (stage plan) and the bytes they read for this batch
+    cuts_c = (ctypes.c_int * 8)()
+    nst = lib.spec_verify_row_stages(1 if w.dtype == "bf16" else 0, w.B, w.D, w.V, cuts_c, 8)
+    if nst < 1:
+        raise RuntimeError(sv.strerror(nst))
+    cuts = [int(cuts_c[i]) for i in range(nst + 1)]
+    fetched = fetched_row_bytes(w, g_al, cuts, tau is not None)
+    kern_gbps = fetched / (kern_ms * 1e-3) / 1e9
 
     # the epilogue (each sequence's window of its W = D+1 latest tokens moved by AL, lengths
     # grown by AL) on the benched batch's outputs, timed alone with events on the same stream
@@ -266,8 +294,8 @@ def main():
         sag = {"us_per_call": sag_us, "k": 5, "factor": 0.5, "draft_rows": draft_rows,
                "gbps": sag_bytes / (sag_us * 1e-6) / 1e9,
                "note": "spec_verify_saguaro_reshape alone (not part of the step): reads every "
-                       "needed draft row once (one workgroup per 32 KB chunk, the chunks' top-5 "
-                       "merged by the row's last chunk) and rewrites its top-5 logits"}
+                       "needed draft row once (one wavefront per 8 KB unit, then one wavefront "
+                       "per row merges the units' candidates) and rewrites its top-5 logits"}
 
     gbps = alg_bytes / (ms_step * 1e-3) / 1e9
     res = {
@@ -290,12 +318,26 @@ def main():
         "pct_of_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
         "logit_rows_per_s": rows / (ms_step * 1e-3),
         "algorithmic_bytes_per_step": alg_bytes,
+        "bytes_note": "hbm_gbps and pct_of_hbm_peak count every logit row the call is given up "
+                      "to L_b (the algorithmic bytes of the workload); the row launches skip the "
+                      "rows past a rejection already known, so they read "
+                      "fetched_row_bytes_per_step (fetched_hbm_gbps over the whole call)",
         "event_ms_per_step": ev_ms_step,
         "mean_accept_len": float(g_al.mean()),
         "parity_unflagged_mismatches": mism,
-        "roofline": {"bound": "hbm", "kernel": "row_kernel", "achieved": kern_gbps,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": kern_gbps / HBM_PEAK_GBPS,
-                     "traffic": read_traffic(args.config, args.seed), "kernel_ms": kern_ms},
+        "fetched_row_bytes_per_step": fetched,
+        "fetched_hbm_gbps": fetched / (ms_step * 1e-3) / 1e9,
+        "row_stages": cuts,
+        "roofline": {"bound": "hbm",
+                     "kernel": "row_kernel" if nst == 1 else
+                               f"row_kernel x{nst} (positions {cuts}) + decide_kernel x{nst - 1}",
+                     "achieved": kern_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": kern_gbps / HBM_PEAK_GBPS,
+                     "traffic": read_traffic(args.config, args.seed), "kernel_ms": kern_ms,
+                     "bytes": fetched,
+                     "note": "row statistics phase of a call (its launches timed as one with HIP "
+                             "events on the launch stream); achieved = the logit bytes those "
+                             "launches read for this batch / their time"},
         "cpu_baseline": None,
         "saguaro_reshape": sag,
         "advance": {"us_per_call": adv_us, "W": W,

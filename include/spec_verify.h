@@ -224,6 +224,15 @@ int spec_verify_advance(const int32_t* accept_len, const int32_t* tokens, int B,
  * holds no buffer), SV_ENODEV without a device, SV_EHIP if the free fails. */
 int spec_verify_release(hipStream_t stream);
 
+/* The row launches spec_verify_bf16 / _f32 / _ws / _noalloc / _threshold make for shape
+ * (B, D, V) and dtype (0 = fp32, 1 = bf16): launch s reads the rows at positions
+ * [cuts[s], cuts[s + 1]) and, for s > 0, skips every row past a sequence's first rejection
+ * among the earlier positions (those rows are not needed: AL and the tokens do not depend on
+ * them). Writes up to max_cuts boundaries (the number of launches plus one) to the host array
+ * cuts and returns the number of launches, or SV_EINVAL. For benchmarks and tests that count
+ * the bytes read; spec_verify_debug reads every row in one launch. */
+int spec_verify_row_stages(int dtype, int B, int D, int V, int* cuts, int max_cuts);
+
 /* Static text for a status code. */
 const char* spec_verify_strerror(int code);
 
@@ -231,9 +240,10 @@ const char* spec_verify_strerror(int code);
 int spec_verify_version(void);
 
 /* Timing hook for benchmarks. spec_verify_profile_start(n) creates n event pairs on the current
- * device; each following call (any entry point, up to n calls) times its row-statistics kernel
+ * device; each following call (any entry point, up to n calls) times its row-statistics phase
  * on the call's stream with one pair: the kernel's own start and end stamps when it is one
- * launch (B <= 32767), else event records around its launches. spec_verify_profile_stop waits for those events,
+ * launch (one stage and B <= 32767), else event records around its row launches and the
+ * decision kernels between them (spec_verify_row_stages). spec_verify_profile_stop waits for those events,
  * writes up to max_out durations in milliseconds to the host array out_ms (may be NULL), the
  * number of recorded calls to *n_recorded, and releases the events. Returns SV_EINVAL if not
  * started (stop) or already started (start), SV_EHIP on a runtime failure. */

@@ -38,6 +38,7 @@ SIGNATURES = {
     "spec_verify_strerror": ([_i], ctypes.c_char_p),
     "spec_verify_version": ([], _i),
     "spec_verify_release": ([_p], _i),
+    "spec_verify_row_stages": ([_i, _i, _i, _i, _p, _i], _i),
     "spec_verify_profile_start": ([_i], _i),
     "spec_verify_profile_stop": ([_p, _i, _p], _i),
 }

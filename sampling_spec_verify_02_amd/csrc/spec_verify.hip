@@ -6,11 +6,13 @@
 // spéculatif"), in-order acceptance up to the first mismatch and AL in [1, 1 + D] from
 // "NVIDIA: öt irányelv ..." (section "Mit csinál a spekulatív dekódolás?").
 //
-// Two to four kernels per call, in stream order: the row kernel, then (item grids of more than
-// one round of resident workgroups only) the outcome kernel, the item kernel, and (then too)
-// the pick kernel. Each hands its results to the next through the kernel boundary; no workgroup
-// waits for another. Inside the item kernel, when its grid is one round, the workgroups of a
-// sequence count their finished items (one atomic per workgroup) and the last one picks.
+// Kernels per call, in stream order: the row kernel (once, or in stages over the positions
+// with a decision kernel between stages, so that rows past a rejection already known are not
+// read), then (item grids of more than one round of resident workgroups only) the outcome
+// kernel, the item kernel, and (then too) the pick kernel. Each hands its results to the next
+// through the kernel boundary; no workgroup waits for another. Inside the item kernel, when its
+// grid is one round, the workgroups of a sequence count their finished items (one atomic per
+// workgroup) and the last one picks.
 // Threshold acceptance runs the same kernels without the draft rows; the epilogue that moves
 // each sequence's token window by AL is a kernel of its own, enqueued after verification.
 //
@@ -37,6 +39,11 @@
 //   token. When every item workgroup of the call is resident at once, the item workgroup that
 //   completes a sequence's count picks (no third kernel); otherwise a pick kernel runs after
 //   the item kernel.
+// * Decision kernel (staged row launches only): one wavefront per sequence evaluates the
+//   positions read so far exactly as the outcome does and stores the first that rejects; the
+//   next row launch skips the rows past it. AL and the tokens do not depend on those rows, and
+//   the outcome, which later reads every row partial up to L, takes the first rejection, so the
+//   stale partials of skipped rows (all past it) never decide anything.
 // * Outcome kernel: only when the item grid takes more than one round of resident workgroups
 //   (large batches). One wavefront per sequence derives the outcome once, between the row and
 //   item kernels, and the item workgroups read it with one load instead of deriving it each.
@@ -120,9 +127,14 @@ struct Params {
   FinPart* fpart;     // [B][nF]
   double* fmass;      // [B][nF] scratch of the pick
   unsigned* done;     // [B] item workgroups finished (when the last one picks)
+  int p_lo;           // first position of this row launch (its grid z covers p_lo ..)
+  const unsigned* dead;  // [B] or null: the first position already known to reject (rows past
+                         // it are not read); 0xffffffff when none is known
+  unsigned* dead_buf;    // [B] where the decision kernel stores it
   int merged;         // 1: the last item workgroup of a sequence does its pick
   int pre;            // 1: the outcome kernel has stored every outcome (item grids of more
                       //    than one round); item workgroups read it instead of deriving it
+  int stage;          // 1: staged row launches that skip the rows past a known rejection
   int thresh;         // 1: threshold acceptance (prefix probability above tau; no draft rows)
   double log_tau;     // ln tau of threshold acceptance (-inf for tau = 0)
   float* dbg_row_stats;  // optional [B][R][2]
@@ -608,9 +620,11 @@ __device__ __forceinline__ OutcomeIn load_outcome(const Params& P, int b, int la
 // Every wavefront that computes the outcome of sequence b from the same partials gets the same
 // bits (fixed combine order). With `write`, the wavefront also stores AL, the tokens other than
 // the final draw's, the outcome words and the debug exports.
+// limit: only positions below it are evaluated (their rows merged); the outcome is then valid
+// for them only (the decision kernel between staged row launches).
 template <typename E>
 __device__ __forceinline__ Outcome seq_outcome(const Params& P, int b, const OutcomeIn& in,
-                                               int lane, bool write) {
+                                               int lane, bool write, int limit = 64) {
   const int D = P.D, R = P.R, nc = P.nchunk;
   // Lane r < R holds row r and combines its chunk partials in order.
   const int r = lane;
@@ -641,7 +655,8 @@ __device__ __forceinline__ Outcome seq_outcome(const Params& P, int b, const Out
   const float iT = 1.f / T;
   const float k2 = kLog2e * iT;
   const int pr = r <= D ? r : r - (D + 1);
-  const bool need = r < R && (r <= D ? pr <= L : (!greedy && !P.thresh && pr < L));
+  const bool need = r < R && pr < limit &&
+                    (r <= D ? pr <= L : (!greedy && !P.thresh && pr < L));
   float m = -INFINITY, s = 0.f, x = 0.f;
   int idx = -1;
   if (need) {
@@ -1291,13 +1306,14 @@ __device__ __forceinline__ void row_workgroup(const Params& P, Shared& sm, int t
   const int c = int(blockIdx.x);
   const int which = int(blockIdx.y) >= P.nb ? 1 : 0;  // 0 target row p, 1 draft row p
   const int b = P.b0 + int(blockIdx.y) - which * P.nb;
-  const int p = int(blockIdx.z);
+  const int p = P.p_lo + int(blockIdx.z);
   const int D = P.D;
   if (P.merged && p == 0 && which == 0 && c == 0 && tid == 0)
     P.done[b] = 0u;                                   // the item kernel counts from zero
   const int L = P.lens ? P.lens[b] : D;
   const float T = P.temperature[b];
   if (!seq_valid(L, D, T)) return;    // invalid length or temperature: nothing is read
+  if (P.dead && unsigned(p) > P.dead[b]) return;   // past a known rejection: not needed
   const bool greedy = (T == 0.f);
   if (which == 0 ? (p <= L) : (!greedy && !P.thresh && p < L))   // rows the method needs
     row_chunk<E>(P, sm, b, p, which, c, L, T, greedy, tid);
@@ -1399,6 +1415,26 @@ __global__ __launch_bounds__(kThreads) void outcome_kernel(Params P) {
   (void)seq_outcome<E>(P, b, in, lane, true);
 }
 
+// Decision kernel between staged row launches: one wavefront per sequence evaluates the
+// positions below `limit` (their rows are all read) exactly as the outcome does, and stores the
+// first of them that rejects (0xffffffff if none does; 0 for a row already marked invalid), so
+// that the next launches do not read the rows past it.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void decide_kernel(Params P, int limit, unsigned* dead) {
+  const int lane = threadIdx.x & 63;
+  const int b = int(blockIdx.x) * kWaves + uniform(int(threadIdx.x >> 6));
+  if (b >= P.B) return;
+  const int L = P.lens ? P.lens[b] : P.D;
+  const float T = P.temperature[b];
+  unsigned d = 0u;
+  if (seq_valid(L, P.D, T)) {
+    const OutcomeIn in = load_outcome(P, b, lane);
+    const Outcome o = seq_outcome<E>(P, b, in, lane, false, limit);
+    d = (o.j < min(L, limit)) ? unsigned(o.j) : 0xffffffffu;
+  }
+  if (lane == 0) dead[b] = d;
+}
+
 template <typename E>
 __global__ __launch_bounds__(kThreads) void pick_kernel(Params P) {
   __shared__ double e2[256];
@@ -1429,7 +1465,7 @@ inline int item_elems(int elem_bytes) { return kRowChunkBytes / elem_bytes / kIt
 // layout serves both dtypes (nF and nchunk are those of the dtype with more).
 struct Layout {
   int nchunk, nF;
-  size_t off_pub, off_rpart, off_fpart, off_fmass, off_done, total;
+  size_t off_pub, off_rpart, off_fpart, off_fmass, off_done, off_dead, total;
 };
 
 inline bool make_layout(int B, int D, int V, Layout& L) {
@@ -1444,6 +1480,7 @@ inline bool make_layout(int B, int D, int V, Layout& L) {
   L.off_fpart = o; o += align256(size_t(B) * L.nF * sizeof(FinPart));
   L.off_fmass = o; o += align256(size_t(B) * L.nF * sizeof(double));
   L.off_done = o;  o += align256(size_t(B) * sizeof(unsigned));
+  L.off_dead = o;  o += align256(size_t(B) * sizeof(unsigned));
   L.total = o;
   return true;
 }
@@ -1509,6 +1546,32 @@ int check_args(const void* t, const void* d, const int32_t* tok, const float* u,
   return SV_OK;
 }
 
+// Row launches of a call: stage s reads positions [cuts[s], cuts[s + 1]). One stage when staging
+// is off (debug exports, which report every row), for D = 0, or when the rows are too few for a
+// stage boundary (a decision kernel and a second row launch, about 7 us) to pay; else a cut at
+// position 1 for D = 1, at 2 for D <= 3 or up to 512 MB of rows, at 1 and 3 beyond. Returns the
+// number of stages.
+constexpr int kMaxStages = 3;
+constexpr size_t kStageMinBytes = size_t(64) << 20, kStageTwoCutBytes = size_t(512) << 20;
+inline int stage_plan(bool stage, int B, int D, int V, int elem_bytes, int* cuts) {
+  const int npos = D + 1;
+  const size_t bytes = size_t(B) * size_t(2 * D + 1) * size_t(V) * size_t(elem_bytes);
+  int n = 0;
+  cuts[n++] = 0;
+  if (stage && npos >= 2 && bytes >= kStageMinBytes) {
+    if (npos == 2) {
+      cuts[n++] = 1;
+    } else if (npos <= 4 || bytes <= kStageTwoCutBytes) {
+      cuts[n++] = 2;
+    } else {
+      cuts[n++] = 1;
+      cuts[n++] = 3;
+    }
+  }
+  cuts[n] = npos;
+  return n;
+}
+
 // Item workgroups resident at once on the current device (0 if unknown).
 template <typename E>
 long long item_capacity() {
@@ -1556,22 +1619,39 @@ int launch(Params& P, hipStream_t stream) {
   constexpr int kRowSlice = 32767, kItemSlice = 65535;
   // Timing: a single row launch takes the events as its own start and end stamps; sliced
   // launches are bracketed by event records.
-  const bool stamped = ev0 && P.B <= kRowSlice;
+  // Staged row launches (stage_plan), each after the first preceded by the decision kernel
+  // for the positions read so far, so that the rows past a known rejection are not read.
+  int cuts[kMaxStages + 1];
+  const int ncut = stage_plan(P.stage != 0, P.B, P.D, P.V, int(sizeof(E)), cuts);
+  const bool stamped = ev0 && P.B <= kRowSlice && ncut == 1;
   if (ev0 && !stamped && hipEventRecord(ev0, stream) != hipSuccess) return SV_EHIP;
-  for (int b0 = 0; b0 < P.B; b0 += kRowSlice) {
-    Params Q = P;
-    Q.b0 = b0;
-    Q.nb = std::min(kRowSlice, P.B - b0);
-    // threshold acceptance reads no draft row: the grid holds the target rows only
-    const dim3 grid(unsigned(Q.nchunk), unsigned((Q.thresh ? 1 : 2) * Q.nb), unsigned(Q.D + 1));
-    if (stamped) {
-      void* args[] = {&Q};
-      if (hipExtLaunchKernel(reinterpret_cast<const void*>(&row_kernel<E>), grid, dim3(kThreads),
-                             args, 0, stream, ev0, ev1, 0) != hipSuccess)
-        return SV_EHIP;
-    } else {
-      hipLaunchKernelGGL(row_kernel<E>, grid, dim3(kThreads), 0, stream, Q);
+  for (int st = 0; st < ncut; ++st) {
+    if (st > 0) {
+      Params Q = P;
+      Q.b0 = 0;
+      Q.nb = P.B;
+      hipLaunchKernelGGL(decide_kernel<E>, dim3(unsigned(picks)), dim3(kThreads), 0, stream, Q,
+                         cuts[st], P.dead_buf);
       if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    }
+    for (int b0 = 0; b0 < P.B; b0 += kRowSlice) {
+      Params Q = P;
+      Q.b0 = b0;
+      Q.nb = std::min(kRowSlice, P.B - b0);
+      Q.p_lo = cuts[st];
+      Q.dead = st > 0 ? P.dead_buf : nullptr;
+      // threshold acceptance reads no draft row: the grid holds the target rows only
+      const dim3 grid(unsigned(Q.nchunk), unsigned((Q.thresh ? 1 : 2) * Q.nb),
+                      unsigned(cuts[st + 1] - cuts[st]));
+      if (stamped) {
+        void* args[] = {&Q};
+        if (hipExtLaunchKernel(reinterpret_cast<const void*>(&row_kernel<E>), grid,
+                               dim3(kThreads), args, 0, stream, ev0, ev1, 0) != hipSuccess)
+          return SV_EHIP;
+      } else {
+        hipLaunchKernelGGL(row_kernel<E>, grid, dim3(kThreads), 0, stream, Q);
+        if (hipGetLastError() != hipSuccess) return SV_EHIP;
+      }
     }
   }
   if (ev1 && !stamped && hipEventRecord(ev1, stream) != hipSuccess) return SV_EHIP;
@@ -1657,8 +1737,10 @@ int run(int dtype, const void* target, const void* draft, const int32_t* tokens,
   P.fpart = reinterpret_cast<FinPart*>(base + lay.off_fpart);
   P.fmass = reinterpret_cast<double*>(base + lay.off_fmass);
   P.done = reinterpret_cast<unsigned*>(base + lay.off_done);
+  P.dead_buf = reinterpret_cast<unsigned*>(base + lay.off_dead);
   P.thresh = thresh ? 1 : 0;
   P.log_tau = log_tau;
+  P.stage = (dbg_stats || dbg_argmax || dbg_logpq) ? 0 : 1;
   P.dbg_row_stats = dbg_stats;
   P.dbg_argmax = dbg_argmax;
   P.dbg_logpq = dbg_logpq;
@@ -2266,7 +2348,16 @@ const char* spec_verify_strerror(int code) {
   }
 }
 
-int spec_verify_version(void) { return 302; }
+int spec_verify_version(void) { return 303; }
+
+int spec_verify_row_stages(int dtype, int B, int D, int V, int* cuts, int max_cuts) {
+  if ((dtype != 0 && dtype != 1) || B <= 0 || D < 0 || D > SV_MAX_D || V <= 0 || !cuts)
+    return SV_EINVAL;
+  int c[sv::kMaxStages + 1];
+  const int n = sv::stage_plan(true, B, D, V, dtype == 1 ? 2 : 4, c);
+  for (int i = 0; i <= n && i < max_cuts; ++i) cuts[i] = c[i];
+  return n;
+}
 
 int spec_verify_release(hipStream_t stream) {
   int dev = 0, count = 0;

@@ -172,3 +172,23 @@ def test_saguaro_bad_arguments():
     assert call(dtype=3) == _lib.SV_EDTYPE
     if torch.cuda.device_count() == 0:
         assert call() == _lib.SV_ENODEV
+
+
+def test_row_stage_plan():
+    """spec_verify_row_stages: boundaries from 0 to D + 1, strictly increasing; one stage for
+    small problems and for D = 0; bad arguments give SV_EINVAL."""
+    lib = _lib.lib()
+    cuts = (ctypes.c_int * 8)()
+    for dt, B, D, V in [(1, 64, 7, 128256), (1, 512, 7, 129280), (1, 256, 3, 128256),
+                        (1, 1024, 1, 129280), (0, 16, 4, 32000), (0, 1, 4, 1024),
+                        (1, 4096, 0, 129280), (0, 3000, 31, 100000)]:
+        n = lib.spec_verify_row_stages(dt, B, D, V, cuts, 8)
+        assert 1 <= n <= 3, (dt, B, D, V, n)
+        c = [cuts[i] for i in range(n + 1)]
+        assert c[0] == 0 and c[-1] == D + 1 and all(a < b for a, b in zip(c, c[1:])), c
+        rows_bytes = B * (2 * D + 1) * V * (2 if dt == 1 else 4)
+        if D == 0 or rows_bytes < (64 << 20):
+            assert n == 1, (dt, B, D, V, c)
+    assert lib.spec_verify_row_stages(5, 64, 7, 100, cuts, 8) == _lib.SV_EINVAL
+    assert lib.spec_verify_row_stages(1, 0, 7, 100, cuts, 8) == _lib.SV_EINVAL
+    assert lib.spec_verify_row_stages(1, 4, 7, 100, None, 8) == _lib.SV_EINVAL
