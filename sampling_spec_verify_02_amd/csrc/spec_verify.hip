@@ -397,8 +397,22 @@ __device__ inline double dpp_scan(double x, double id, Op op) {
   return x;
 }
 
+// The sum scan: the row shifts read 0 from outside the row (bound_ctrl) instead of an identity
+// moved into the destination first; the same additions in the same order as dpp_scan.
+template <int CTRL>
+__device__ inline double dpp_shr_zero(double x) {
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), CTRL, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), CTRL, 0xf, 0xf, true);
+  return __hiloint2double(hi, lo);
+}
 __device__ inline double dpp_scan_add(double x) {
-  return dpp_scan(x, 0.0, [](double u, double v) { return u + v; });
+  x += dpp_shr_zero<0x111>(x);                // row_shr:1
+  x += dpp_shr_zero<0x112>(x);                // row_shr:2
+  x += dpp_shr_zero<0x114>(x);                // row_shr:4
+  x += dpp_shr_zero<0x118>(x);                // row_shr:8
+  x += dpp_double<0x142, 0xa>(x, 0.0);        // row_bcast:15 into rows 1 and 3
+  x += dpp_double<0x143, 0xc>(x, 0.0);        // row_bcast:31 into rows 2 and 3
+  return x;
 }
 // value of lane l (wave-uniform l)
 __device__ inline double readlane(double x, int l) {
@@ -1238,20 +1252,19 @@ __device__ __forceinline__ void item_sums(const Params& P, int b, int f, const D
       }
     }
   }
-  const auto add = [](double u, double v) { return u + v; };
   const auto mn = [](double u, double v) { return fmin(u, v); };
   const auto mx = [](double u, double v) { return fmax(u, v); };
 #pragma unroll
   for (int k = 0; k < KB; ++k) {
-    kat[k] = dpp_scan(kat[k], 0.0, add);
-    if (w.residual) kad[k] = dpp_scan(kad[k], 0.0, add);
+    kat[k] = dpp_scan_add(kat[k]);
+    if (w.residual) kad[k] = dpp_scan_add(kad[k]);
   }
   if (w.residual) {
-    st = dpp_scan(st, 0.0, add);
-    sd = dpp_scan(sd, 0.0, add);
+    st = dpp_scan_add(st);
+    sd = dpp_scan_add(sd);
     if (any_band) {                    // else every lane holds the identities already
-      bt = dpp_scan(bt, 0.0, add);
-      bd = dpp_scan(bd, 0.0, add);
+      bt = dpp_scan_add(bt);
+      bd = dpp_scan_add(bd);
       dmin = dpp_scan(dmin, INFINITY, mn);
       dmax = dpp_scan(dmax, -INFINITY, mx);
     }
