@@ -2069,13 +2069,15 @@ __global__ __launch_bounds__(kThreads) void reshape_merge_kernel(E* draft, const
   int mine = -1;
   bool done = false;
   if (ncand <= 8 * 64) {
-    // lane l takes slots 8 l .. 8 l + 7: half a unit's slots, so that every group of eight
-    // lanes holds the hits of four units (a unit's empty slots are its last ones)
+    // lane l takes slots s l .. s l + s - 1, s = ceil(ncand / 64): the slots spread over every
+    // lane, so that each group of eight lanes holds candidates and the k-th largest group max
+    // (below which no candidate can be in the top k, whatever the grouping) is a real bound
+    const int sp = (ncand + 63) >> 6;
     unsigned long long w[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const int q = lane * 8 + t;
-      w[t] = q < ncand ? rc[q] : pack_cand(0.f, -1);
+      const int q = lane * sp + t;
+      w[t] = (t < sp && q < ncand) ? rc[q] : pack_cand(0.f, -1);
     }
     float m = -INFINITY;
 #pragma unroll
