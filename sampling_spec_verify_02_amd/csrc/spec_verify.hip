@@ -1467,9 +1467,9 @@ __global__ __launch_bounds__(kThreads) void pick_kernel(Params P) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Final-draw item length for a dtype: kItemsPerChunk items per row chunk, so that the
-// wavefronts of one position's row workgroups (kWaves per workgroup, 2 * nchunk workgroups per
-// sequence) outnumber the items of the whole batch.
+// Final-draw item length for a dtype: kItemsPerChunk items per row chunk, 4 KB of each final
+// row (2048 bf16 or 1024 fp32 logits, four blocks of 512): one wavefront's item. Half as long
+// measured slower (twice the items for every pick), twice as long needs more registers.
 inline int item_elems(int elem_bytes) { return kRowChunkBytes / elem_bytes / kItemsPerChunk; }
 
 // Workspace: [outcome words B][row partials][final-draw partials][pick scratch][item counters B].
