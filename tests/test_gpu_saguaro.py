@@ -34,7 +34,10 @@ def _reshape_on_gpu(w, factor, k):
     # last chunk, a chunk smaller than k
     ("c3", dict(B=6, V=1001), 0.5, 5), ("c3", dict(B=4, V=200003), 0.3, 8),
     ("c2", dict(B=4, V=70001), 0.7, 4), ("c3", dict(B=5, V=2 * 16384 + 3), 0.5, 8),
-    ("c2", dict(B=5, V=3 * 8192 + 5), 0.5, 8)])
+    ("c2", dict(B=5, V=3 * 8192 + 5), 0.5, 8),
+    # merge slot counts that spread 2 and 3 per lane (96 and 160 slots; k = 8 leaves lane groups
+    # without candidates)
+    ("c2", dict(B=4, V=5 * 2048 + 7), 0.5, 8), ("c3", dict(B=4, V=9 * 4096 + 1), 0.5, 5)])
 def test_reshape_matches_oracle(cfg, kw, factor, k):
     w = make(cfg, 70, **kw)
     if cfg == "c5":
