@@ -54,3 +54,33 @@ def test_rows_past_a_known_rejection_are_not_read(cfg, kw):
     al, toks = G.run(w)
     G.compare(ref, al, toks, f"{cfg} poisoned")
     assert np.array_equal(al[~ref.flagged], ref.accept_len[~ref.flagged])
+
+
+def test_staged_batches_beyond_one_grid_slice():
+    """40,000 sequences, D = 3, V = 256 bf16 (143 MB of rows): staged row launches, each in two
+    slices of sequences, the decision kernel over the whole batch between them, and item and
+    outcome grids of more than one round. Drafts close to the target, so that many sequences
+    reach the second launch."""
+    from oracle import verify
+    from workloads.gen import bf16_decode, bf16_round
+    rng = np.random.default_rng(22)
+    B, D, V = 40000, 3, 256
+    tgt32 = (rng.standard_normal((B, D + 1, V)) * 2.0).astype(np.float32)
+    drf32 = tgt32[:, :D] + (rng.standard_normal((B, D, V)) * 0.3).astype(np.float32)
+    tgt, drf = bf16_round(tgt32), bf16_round(drf32)
+    toks = rng.integers(0, V, (B, D)).astype(np.int32)
+    u = rng.random((B, D + 1), dtype=np.float32)
+    T = np.ones(B, np.float32)
+    c = (ctypes.c_int * 8)()
+    n = _lib.lib().spec_verify_row_stages(1, B, D, V, c, 8)
+    cuts = [c[i] for i in range(n + 1)]
+    print(f"B={B} D={D} V={V} bf16 stages {cuts}", flush=True)
+    assert len(cuts) > 2, "the batch should be staged"
+    ref = verify(bf16_decode(tgt), bf16_decode(drf), toks, None, u, T)
+    assert np.mean(ref.accept_len >= 3) > 0.1      # the second launch has rows to read
+    dev = G.device()
+    al, out = sv.spec_verify(G.logits_to_dev(tgt, "bf16", dev), G.logits_to_dev(drf, "bf16", dev),
+                             torch.from_numpy(toks).to(dev), None, torch.from_numpy(u).to(dev),
+                             torch.from_numpy(T).to(dev))
+    torch.cuda.synchronize()
+    G.compare(ref, al.cpu().numpy(), out.cpu().numpy(), "B=40000 staged")
