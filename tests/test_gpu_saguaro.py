@@ -158,3 +158,18 @@ def test_reshape_temperature_extremes(T):
     got = _reshape_on_gpu(w, 0.5, 5)
     want = reshape_draft(w.draft, w.dtype, None, w.temperature, 0.5, 5)
     assert np.array_equal(got, want)
+
+
+def test_reshape_batches_beyond_one_grid_slice():
+    """70,000 sequences: the unit and merge grids are launched in two slices of sequences; each
+    slice must write its own rows and read its own candidate slots."""
+    rng = np.random.default_rng(23)
+    B, D, V = 70000, 1, 100
+    draft = (rng.standard_normal((B, D, V)) * 2.0).astype(np.float32)
+    T = np.ones(B, np.float32)
+    dev = G.device()
+    d = torch.from_numpy(draft).to(dev)
+    sv.spec_verify_saguaro_reshape(d, None, torch.from_numpy(T).to(dev), 0.5, 5)
+    torch.cuda.synchronize()
+    want = reshape_draft(draft, "f32", None, T, 0.5, 5)
+    assert np.array_equal(d.cpu().numpy().view(np.uint8), want.view(np.uint8))
