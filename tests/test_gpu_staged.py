@@ -25,9 +25,10 @@ def _cuts(w):
 
 
 # c3: one cut at 2; c4: one cut at 2 of four positions; mtp: one cut at 1; c5 at B=160 (620 MB
-# of rows, ragged lengths): two cuts, at 1 and 3
+# of rows, ragged lengths): two cuts, at 1 and 3; c2's generator at B=32 D=7 V=128256: fp32 rows
+# (246 MB), one cut at 2
 @pytest.mark.parametrize("cfg,kw", [("c3", {}), ("c4", {}), ("mtp", dict(B=512)),
-                                    ("c5", dict(B=160))])
+                                    ("c5", dict(B=160)), ("c2", dict(B=32, D=7, V=128256))])
 def test_rows_past_a_known_rejection_are_not_read(cfg, kw):
     w = make(cfg, 41, **kw)
     cuts = _cuts(w)
