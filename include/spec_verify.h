@@ -240,13 +240,13 @@ const char* spec_verify_strerror(int code);
 int spec_verify_version(void);
 
 /* Timing hook for benchmarks. spec_verify_profile_start(n) creates n event pairs on the current
- * device; each following call (any entry point, up to n calls) times its row-statistics phase
- * on the call's stream with one pair: the kernel's own start and end stamps when it is one
- * launch (one stage and B <= 32767), else event records around its row launches and the
- * decision kernels between them (spec_verify_row_stages). spec_verify_profile_stop waits for those events,
- * writes up to max_out durations in milliseconds to the host array out_ms (may be NULL), the
- * number of recorded calls to *n_recorded, and releases the events. Returns SV_EINVAL if not
- * started (stop) or already started (start), SV_EHIP on a runtime failure. */
+ * device; each following row-kernel launch (any entry point, in call order; a call makes one
+ * launch per stage of spec_verify_row_stages and per slice of 32767 sequences) takes one pair as
+ * its own start and end stamps, until the n pairs are used. The decision kernels between stages
+ * and the later kernels of a call are not timed. spec_verify_profile_stop waits for those events,
+ * writes up to max_out durations in milliseconds, in launch order, to the host array out_ms (may
+ * be NULL), the number of recorded launches to *n_recorded, and releases the events. Returns
+ * SV_EINVAL if not started (stop) or already started (start), SV_EHIP on a runtime failure. */
 int spec_verify_profile_start(int max_calls);
 int spec_verify_profile_stop(float* out_ms, int max_out, int* n_recorded);
 

@@ -1514,7 +1514,7 @@ struct DeviceWorkspace {
 std::mutex g_ws_mutex;
 std::map<std::pair<int, hipStream_t>, DeviceWorkspace> g_ws;
 
-struct Profile {        // optional timing of the kernel: one event pair per call
+struct Profile {        // optional timing of the row kernel: one event pair per row launch
   std::vector<hipEvent_t> begin, end;
   int used = 0;
   bool armed = false;
@@ -1618,26 +1618,15 @@ int launch(Params& P, hipStream_t stream) {
   // round, one wavefront per sequence), rather than once per item workgroup.
   P.pre = P.merged ? 0 : 1;
 
-  hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  {
-    std::lock_guard<std::mutex> g(g_prof_mutex);
-    if (g_prof.armed && g_prof.used < int(g_prof.begin.size())) {
-      ev0 = g_prof.begin[size_t(g_prof.used)];
-      ev1 = g_prof.end[size_t(g_prof.used)];
-      ++g_prof.used;
-    }
-  }
   // A grid's y dimension holds at most 65535 workgroups: larger batches launch in slices of
   // sequences (stream-ordered, so each kernel still sees every earlier kernel's results).
   constexpr int kRowSlice = 32767, kItemSlice = 65535;
-  // Timing: a single row launch takes the events as its own start and end stamps; sliced
-  // launches are bracketed by event records.
+  // Timing (profile hook armed): each row launch takes an event pair as its own start and end
+  // stamps.
   // Staged row launches (stage_plan), each after the first preceded by the decision kernel
   // for the positions read so far, so that the rows past a known rejection are not read.
   int cuts[kMaxStages + 1];
   const int ncut = stage_plan(P.stage != 0, P.B, P.D, P.V, int(sizeof(E)), cuts);
-  const bool stamped = ev0 && P.B <= kRowSlice && ncut == 1;
-  if (ev0 && !stamped && hipEventRecord(ev0, stream) != hipSuccess) return SV_EHIP;
   for (int st = 0; st < ncut; ++st) {
     if (st > 0) {
       Params Q = P;
@@ -1656,7 +1645,16 @@ int launch(Params& P, hipStream_t stream) {
       // threshold acceptance reads no draft row: the grid holds the target rows only
       const dim3 grid(unsigned(Q.nchunk), unsigned((Q.thresh ? 1 : 2) * Q.nb),
                       unsigned(cuts[st + 1] - cuts[st]));
-      if (stamped) {
+      hipEvent_t ev0 = nullptr, ev1 = nullptr;
+      {
+        std::lock_guard<std::mutex> g(g_prof_mutex);
+        if (g_prof.armed && g_prof.used < int(g_prof.begin.size())) {
+          ev0 = g_prof.begin[size_t(g_prof.used)];
+          ev1 = g_prof.end[size_t(g_prof.used)];
+          ++g_prof.used;
+        }
+      }
+      if (ev0) {
         void* args[] = {&Q};
         if (hipExtLaunchKernel(reinterpret_cast<const void*>(&row_kernel<E>), grid,
                                dim3(kThreads), args, 0, stream, ev0, ev1, 0) != hipSuccess)
@@ -1667,7 +1665,6 @@ int launch(Params& P, hipStream_t stream) {
       }
     }
   }
-  if (ev1 && !stamped && hipEventRecord(ev1, stream) != hipSuccess) return SV_EHIP;
   if (P.pre) {
     hipLaunchKernelGGL(outcome_kernel<E>, dim3(unsigned(picks)), dim3(kThreads), 0, stream, P);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
